@@ -1,0 +1,171 @@
+// lpc_device.hpp -- device-side building blocks for the gfx950 FP8 codec kernels.
+//
+// Element layout shared by every kernel: one lane owns a "granule" of 16
+// contiguous elements, so the 8 adjacent lanes of a wavefront-aligned group
+// own one 128-element scale block.  A lane moves its granule with 16-byte
+// vector loads/stores (fp32: 4, bf16: 2, codes: 1) and the block's absmax is
+// reduced across its 8 lanes with DPP moves inside the wavefront (no LDS).
+//
+// FP8 is OCP E4M3FN (the gfx950 native FP8 format): the conversions below use
+// the gfx950 instructions v_cvt_pk_fp8_f32 (round to nearest even) and
+// v_cvt_pk_f32_fp8 (exact).  Values are clamped to +-448 first with v_med3,
+// which makes the conversion saturating whatever the instruction does on
+// overflow.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace lpc {
+
+constexpr int kBlock = 128;        // elements per scale
+constexpr int kGranule = 16;       // elements per lane
+constexpr int kLanesPerBlock = kBlock / kGranule;  // 8
+constexpr float kFp8Max = 448.0f;
+constexpr int kMaxRanks = 8;
+
+struct RankCodes {
+    const uint8_t* codes[kMaxRanks];
+    const float* scales[kMaxRanks];
+};
+
+struct RankBufs {
+    const void* p[kMaxRanks];
+};
+
+// ---------------------------------------------------------------------------
+// cross-lane max over the 8-lane group of a 128-element block (DPP)
+// ---------------------------------------------------------------------------
+
+// quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror
+// (lane i <-> 7-i inside each 8-lane half row: joins the two quads).
+__device__ __forceinline__ float group8_max(float v) {
+    int x = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 codec
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float clamp448(float q) {
+    return __builtin_amdgcn_fmed3f(q, -kFp8Max, kFp8Max);
+}
+
+// four already-scaled values -> four codes in one dword (element 0 in byte 0)
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+    return (uint32_t)w;
+}
+
+// codes of fl32(v[j] / s) for a granule; s > 0.  The division is IEEE
+// (correctly rounded, denormals kept), as the quantization rule requires.
+__device__ __forceinline__ uint4 encode16(const float (&v)[kGranule], float s) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        w[j] = encode4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// exact decode of the four codes in a dword
+__device__ __forceinline__ void decode4(uint32_t w, float* out) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[0] = lo[0];
+    out[1] = lo[1];
+    out[2] = hi[0];
+    out[3] = hi[1];
+}
+
+// d[j] = fl32(E4M3(code j) * s)
+__device__ __forceinline__ void dequant16(uint4 c, float s, float (&d)[kGranule]) {
+    decode4(c.x, d + 0);
+    decode4(c.y, d + 4);
+    decode4(c.z, d + 8);
+    decode4(c.w, d + 12);
+#pragma unroll
+    for (int j = 0; j < kGranule; ++j) d[j] = d[j] * s;
+}
+
+// Blockwise quantization of a granule whose 8-lane group forms one block:
+// returns the codes and sets *scale (identical in all 8 lanes).
+__device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], float* scale) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kGranule; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group8_max(amax);
+    const float s = amax / kFp8Max;
+    *scale = s;
+    if (s == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
+    return encode16(v, s);
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two floats -> two bf16 (round to nearest even) packed low/high
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 ha = (__bf16)a;
+    __bf16 hb = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// granule loads / stores
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load16(const float* __restrict__ p, float (&v)[kGranule]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float4 t = q[j];
+        v[4 * j] = t.x;
+        v[4 * j + 1] = t.y;
+        v[4 * j + 2] = t.z;
+        v[4 * j + 3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&v)[kGranule]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint4 t = q[j];
+        uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[8 * j + 2 * k] = bf16lo(w[k]);
+            v[8 * j + 2 * k + 1] = bf16hi(w[k]);
+        }
+    }
+}
+
+__device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[kGranule]) {
+    float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+}
+
+__device__ __forceinline__ void store16(uint16_t* __restrict__ p, const float (&v)[kGranule]) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        q[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
+                          pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
+}
+
+}  // namespace lpc

@@ -1,0 +1,171 @@
+"""The C ABI on the host, no GPU needed: the library loads, exports every function
+include/lpc.h declares, and rejects bad arguments with the documented status
+before touching the HIP runtime.
+
+The pointers used here are fake addresses (aligned or not); every call below
+is one that validation must refuse, so nothing is ever dereferenced or
+launched.
+"""
+import ctypes
+import re
+
+import pytest
+
+from fp8_precision_allreduce_amd import lpc
+
+OK, NULL, SHAPE, RANKS, DTYPE, ALIGN, HIP = range(7)
+A = 0x10000        # a fake 16-byte-aligned device address
+B = 0x10008        # a fake misaligned one
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch
+
+    # Fake addresses must never reach a kernel; if a call here wrongly passed
+    # validation on a machine with a GPU it would launch on them.  These
+    # checks are for the GPU-less host only.
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-pointer ABI checks run only where no GPU is visible")
+    return lpc.lib()
+
+
+def arr(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def test_exports_every_declared_function(L):
+    names = lpc.header_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(lpc.SIGNATURES) | {"lpc_status_string", "lpc_abi_version"} == set(names)
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define LPC_ABI_VERSION (\d+)", open(lpc.HEADER).read())
+    assert lpc.lpc_abi_version() == int(m.group(1))
+
+
+def test_status_strings(L):
+    for i, name in enumerate(lpc.STATUS):
+        assert lpc.lpc_status_string(i).startswith(name)
+    assert "unknown" in lpc.lpc_status_string(99)
+
+
+def test_quantize_errors(L):
+    f = L.lpc_quantize_fp8
+    assert f(A, 7, 128, A, A, None) == DTYPE
+    assert f(A, F32, 0, None, None, None) == OK          # n == 0: no-op, no pointer needed
+    assert f(None, F32, 128, A, A, None) == NULL
+    assert f(A, F32, 128, None, A, None) == NULL
+    assert f(A, F32, 128, A, None, None) == NULL
+    assert f(B, F32, 128, A, A, None) == ALIGN
+    assert f(A, BF16, 128, B, A, None) == ALIGN
+    assert f(A, F32, 128, A, A + 4, None) == ALIGN
+    assert f(A, F32, 100, A, A, None) == SHAPE
+    assert f(A, F32, 129, A, A, None) == SHAPE
+    assert f(A, F32, (1 << 38) + 128, A, A, None) == SHAPE
+
+
+@pytest.mark.parametrize("name", ["lpc_reduce_scatter_chunk"])
+def test_reduce_scatter_chunk_errors(L, name):
+    f = getattr(L, name)
+    c4, s4 = arr(A, A, A, A), arr(A, A, A, A)
+    assert f(c4, s4, 0, 0, 512, A, A, None) == RANKS
+    assert f(c4, s4, 9, 0, 512, A, A, None) == RANKS
+    assert f(c4, s4, 4, 4, 512, A, A, None) == RANKS
+    assert f(c4, s4, 4, -1, 512, A, A, None) == RANKS
+    assert f(c4, s4, 4, 0, 0, None, None, None) == OK
+    assert f(None, s4, 4, 0, 512, A, A, None) == NULL
+    assert f(arr(A, A, None, A), s4, 4, 0, 512, A, A, None) == NULL
+    assert f(c4, arr(A, None, A, A), 4, 0, 512, A, A, None) == NULL
+    assert f(c4, s4, 4, 0, 512, None, A, None) == NULL
+    assert f(arr(A, A, A, B), s4, 4, 0, 512, A, A, None) == ALIGN
+    assert f(c4, s4, 4, 0, 512, A, B, None) == ALIGN
+    assert f(c4, s4, 4, 0, 256, A, A, None) == SHAPE      # not a multiple of 128*N
+    assert f(c4, s4, 4, 0, 640, A, A, None) == SHAPE
+
+
+def test_reduce_scatter_errors(L):
+    f = L.lpc_reduce_scatter
+    c2, s2 = arr(A, A), arr(A, A)
+    assert f(c2, s2, 2, 0, 256, A, 3, None) == DTYPE
+    assert f(c2, s2, 2, 2, 256, A, F32, None) == RANKS
+    assert f(c2, s2, 2, 0, 256, None, F32, None) == NULL
+    assert f(c2, s2, 2, 0, 256, B, BF16, None) == ALIGN
+    assert f(c2, s2, 2, 0, 384, A, F32, None) == SHAPE
+
+
+def test_allgather_errors(L):
+    f = L.lpc_allgather_dequant
+    c2, s2 = arr(A, A), arr(A, A)
+    assert f(c2, s2, 2, 256, A, 2, None) == DTYPE
+    assert f(c2, s2, 0, 256, A, F32, None) == RANKS
+    assert f(c2, s2, 2, 0, None, F32, None) == OK
+    assert f(c2, arr(None, A), 2, 256, A, F32, None) == NULL
+    assert f(c2, s2, 2, 256, B, F32, None) == ALIGN
+    assert f(c2, s2, 2, 128, A, F32, None) == SHAPE
+
+
+def test_fused_errors(L):
+    f = L.lpc_rs_ag_fused
+    c2, s2 = arr(A, A), arr(A, A)
+    assert f(c2, s2, 2, 0, 256, A, A, c2, s2, A, 5, None) == DTYPE
+    assert f(c2, s2, 2, 2, 256, A, A, c2, s2, A, F32, None) == RANKS
+    # the peer arrays' own-rank entry may be NULL ...
+    assert f(c2, s2, 2, 0, 384, A, A, arr(None, A), arr(None, A), A, F32, None) == SHAPE
+    # ... but no other entry
+    assert f(c2, s2, 2, 0, 256, A, A, arr(A, None), arr(A, A), A, F32, None) == NULL
+    assert f(c2, s2, 2, 1, 256, A, A, arr(None, A), arr(A, A), A, F32, None) == NULL
+    assert f(c2, s2, 2, 0, 256, A, A, arr(None, A), arr(None, A), None, F32, None) == NULL
+    assert f(c2, s2, 2, 0, 256, A, A, arr(None, B), arr(None, A), A, F32, None) == ALIGN
+    assert f(c2, s2, 2, 0, 256, A, B, arr(None, A), arr(None, A), A, F32, None) == ALIGN
+
+
+def test_dda_errors(L):
+    f = L.dda_flat_reduce
+    assert f(arr(A, A), 0, 16, A, None) == RANKS
+    assert f(arr(A, A), 2, 0, None, None) == OK
+    assert f(arr(A, None), 2, 16, A, None) == NULL
+    assert f(arr(A, B), 2, 16, A, None) == ALIGN
+    assert f(arr(A, A), 2, (1 << 38) + 1, A, None) == SHAPE
+    g = L.dda_tree_reduce_scatter
+    assert g(arr(A, A), 9, 2, 0, 32, A, None) == DTYPE
+    assert g(arr(A, A), F32, 2, 3, 32, A, None) == RANKS
+    assert g(arr(A, A), F32, 2, 0, 24, A, None) == SHAPE
+    h = L.dda_tree_allgather
+    assert h(arr(A, A), BF16, 2, 32, None, None) == NULL
+    assert h(arr(A, A), BF16, 2, 40, A, None) == SHAPE
+
+
+def test_a2av_errors(L):
+    f = L.lpc_a2av_route
+    assert f(A, 16, 0, A, A, A, None) == RANKS
+    assert f(A, 0, 8, None, None, None, None) == OK
+    assert f(A, 16, 8, A, None, A, None) == NULL
+    assert f(A, 16, 8, A, A, B, None) == ALIGN
+    assert f(A, 1 << 31, 8, A, A, A, None) == SHAPE
+    g = L.lpc_quantize_fp8_rows
+    assert g(A, 4, 16, 128, A, A, A, None) == DTYPE
+    assert g(A, BF16, 16, 0, A, A, A, None) == OK
+    assert g(A, BF16, 16, 128, None, A, A, None) == NULL
+    assert g(A, BF16, 16, 128, A, A, B, None) == ALIGN
+    assert g(A, BF16, 16, 100, A, A, A, None) == SHAPE
+    d = L.lpc_dequantize_fp8
+    assert d(A, A, 128, A, 2, None) == DTYPE
+    assert d(A, None, 128, A, F32, None) == NULL
+    assert d(A, A, 128, B, F32, None) == ALIGN
+    assert d(A, A, 130, A, F32, None) == SHAPE
+    e = L.lpc_e4m3_encode
+    assert e(None, 5, A, None) == NULL
+    assert e(A, 5, B, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No silent fallback: a missing liblpc.so is an error, not a CPU path."""
+    monkeypatch.setattr(lpc, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(lpc, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        lpc.lib()

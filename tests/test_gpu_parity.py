@@ -1,0 +1,471 @@
+"""GPU parity: every HIP entry point against the CPU oracle, bit for bit.
+
+The bar is byte equality everywhere (codes, scales, FP32 and bf16 outputs,
+routing): both sides round every multiply and add separately in IEEE binary32
+(no contraction), divide with a correctly rounded division, and use the same
+E4M3 and bf16 round-to-nearest-even rules, so there is exactly one correct
+result.  All calls go through the C ABI (ctypes binding); inputs are the
+seeded generators' buffers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_precision_allreduce_amd import inputs
+from fp8_precision_allreduce_amd import lpc
+
+pytestmark = pytest.mark.gpu
+BLOCK = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lpc.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# -- host <-> device helpers --------------------------------------------------
+
+def to_dev(a: np.ndarray, dev) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def f32bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def assert_same(gpu: np.ndarray, ref: np.ndarray, what: str):
+    if gpu.dtype == np.float32:
+        gpu, ref = f32bits(gpu), f32bits(ref)
+    bad = np.nonzero(gpu.reshape(-1) != ref.reshape(-1))[0]
+    assert bad.size == 0, "%s: %d mismatches, first at %s: gpu %s ref %s" % (
+        what, bad.size, bad[:4], gpu.reshape(-1)[bad[:4]], ref.reshape(-1)[bad[:4]])
+
+
+def gpu_quantize(x_dev):
+    n = x_dev.numel()
+    codes = torch.empty(n, dtype=torch.uint8, device=x_dev.device)
+    scales = torch.empty(n // BLOCK, dtype=torch.float32, device=x_dev.device)
+    lpc.lpc_quantize_fp8(x_dev, codes, scales)
+    return codes, scales
+
+
+def gpu_lp_allreduce(xs_dev, out_dtype, fused=True):
+    """All N ranks' steps on one GPU: quantize every rank, RS every chunk, then each
+    rank's all-gather (fused kernel for the fused path)."""
+    N = len(xs_dev)
+    n = xs_dev[0].numel()
+    C = n // N
+    dev = xs_dev[0].device
+    q = [gpu_quantize(x) for x in xs_dev]
+    codes = [c for c, _ in q]
+    scales = [s for _, s in q]
+    cc = [torch.empty(C, dtype=torch.uint8, device=dev) for _ in range(N)]
+    cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    for r in range(N):
+        lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
+    outs = []
+    for r in range(N):
+        out = torch.empty(n, dtype=out_dtype, device=dev)
+        if fused:
+            own_c = torch.empty(C, dtype=torch.uint8, device=dev)
+            own_s = torch.empty(C // BLOCK, dtype=torch.float32, device=dev)
+            peers_c = [None if p == r else cc[p] for p in range(N)]
+            peers_s = [None if p == r else cs[p] for p in range(N)]
+            lpc.lpc_rs_ag_fused(codes, scales, r, own_c, own_s, peers_c, peers_s, out)
+            assert torch.equal(own_c, cc[r]) and torch.equal(own_s.view(torch.int32), cs[r].view(torch.int32))
+        else:
+            lpc.lpc_allgather_dequant(cc, cs, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    return dict(codes=codes, scales=scales, chunk_codes=cc, chunk_scales=cs, outs=outs)
+
+
+def compare_allreduce(res, ref, what):
+    N = len(res["codes"])
+    for r in range(N):
+        assert_same(to_host(res["codes"][r]), ref["codes"][r], "%s codes[%d]" % (what, r))
+        assert_same(to_host(res["scales"][r]), ref["scales"][r], "%s scales[%d]" % (what, r))
+        assert_same(to_host(res["chunk_codes"][r]), ref["chunk_codes"][r], "%s chunk codes[%d]" % (what, r))
+        assert_same(to_host(res["chunk_scales"][r]), ref["chunk_scales"][r], "%s chunk scales[%d]" % (what, r))
+    for r in range(N):
+        assert_same(to_host(res["outs"][r]), ref["out"], "%s out on rank %d" % (what, r))
+
+
+# -- codec ----------------------------------------------------------------------
+
+def _codec_values():
+    table = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float32)
+    mids = ((table[:-1].astype(np.float64) + table[1:]) / 2).astype(np.float32)
+    base = np.concatenate([table, mids, np.float32([464.0, 480.0, 500.0, 1e6, 3.4e38, 2.0 ** -10,
+                                                     2.0 ** -11, 1e-40, 1.4e-45, 2.0 ** -126])])
+    vals = [base]
+    for k in range(1, 9):
+        vals.append((f32bits(base) + np.uint32(k)).view(np.float32))
+        vals.append((f32bits(base[base > 0]) - np.uint32(k)).view(np.float32))
+    g = np.random.Generator(np.random.PCG64(101))
+    rnd = g.integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    vals.append(rnd[np.isfinite(rnd)])
+    vals.append(g.uniform(-470, 470, 1 << 20).astype(np.float32))
+    v = np.concatenate(vals).astype(np.float32)
+    v = v[np.isfinite(v)]
+    return np.concatenate([v, -v, np.float32([0.0, -0.0])])
+
+
+def test_e4m3_encode_matches_oracle(dev, orc):
+    v = _codec_values()
+    say("e4m3 encode, %d values (+ragged tail)" % v.size)
+    for n in (v.size, 7, 1):
+        codes = torch.empty(n, dtype=torch.uint8, device=dev)
+        lpc.lpc_e4m3_encode(to_dev(v[:n], dev), codes)
+        assert_same(to_host(codes), orc.e4m3_encode(v[:n]), "encode n=%d" % n)
+
+
+@pytest.mark.parametrize("lo_exp,hi_exp", [(-12, -5), (7, 10)])
+def test_e4m3_encode_every_float_in_binades(dev, orc, lo_exp, hi_exp):
+    """Every float32 pattern with exponent in [lo, hi): the E4M3 subnormal/tie region
+    and the top binade with saturation."""
+    lo = np.uint32(f32bits(np.float32([2.0 ** lo_exp]))[0])
+    hi = np.uint32(f32bits(np.float32([2.0 ** hi_exp]))[0])
+    v = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
+    say("e4m3 encode every float in [2^%d, 2^%d): %d values" % (lo_exp, hi_exp, v.size))
+    codes = torch.empty(v.size, dtype=torch.uint8, device=dev)
+    xd = to_dev(v, dev)
+    lpc.lpc_e4m3_encode(xd, codes)
+    assert_same(to_host(codes), orc.e4m3_encode(v), "encode +")
+    lpc.lpc_e4m3_encode(-xd, codes)
+    assert_same(to_host(codes), orc.e4m3_encode(-v), "encode -")
+
+
+# -- quantize / dequantize ---------------------------------------------------------------
+
+def _edge_blocks():
+    """Blocks that exercise the special cases: zeros of both signs, a scale that
+    underflows, f32-denormal scales (saturating codes), one huge outlier, exact
+    power-of-two values, a block of one repeated value."""
+    g = np.random.Generator(np.random.PCG64(103))
+    b = []
+    b.append(np.zeros(BLOCK, np.float32))
+    b.append(np.full(BLOCK, -0.0, np.float32))
+    z = np.zeros(BLOCK, np.float32)
+    z[7] = np.float32(1e-45)
+    b.append(z)
+    b.append((np.float32(2.0 ** -149) * g.integers(-700, 701, BLOCK)).astype(np.float32))
+    b.append((np.float32(2.0 ** -140) * g.integers(-5, 6, BLOCK)).astype(np.float32))
+    o = inputs.normal_f32(g, BLOCK, 1.0)
+    o[3] = np.float32(1e30)
+    b.append(o)
+    b.append(np.ldexp(np.float32(1), g.integers(-30, 30, BLOCK)).astype(np.float32))
+    b.append(np.full(BLOCK, np.float32(3.0), np.float32))
+    b.append(inputs.normal_f32(g, BLOCK, 1e-30))
+    b.append(inputs.normal_f32(g, BLOCK, 1e30))
+    return np.concatenate(b)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_quantize_matches_oracle(dev, orc, bf16):
+    cases = {
+        "cfg1_rank0": inputs.rank_buffer(1, 0),
+        "ragged_37blocks": inputs.rank_buffer(1, 1, 37 * BLOCK),
+        "one_block": inputs.rank_buffer(1, 2, BLOCK),
+        "edge_blocks": _edge_blocks(),
+        "cfg3_sample": inputs.rank_buffer(3, 0, 33 * 4096 + 5 * BLOCK),
+    }
+    for name, x in cases.items():
+        if bf16:
+            x = inputs.truncate_to_bf16(x)
+        say("quantize", name, "bf16" if bf16 else "f32", x.size)
+        codes, scales = gpu_quantize(to_dev(x, dev))
+        rc, rs = orc.quantize(x, bf16=bf16)
+        assert_same(to_host(codes), rc, name + " codes")
+        assert_same(to_host(scales), rs, name + " scales")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_dequantize_matches_oracle(dev, orc, bf16):
+    x = np.concatenate([inputs.rank_buffer(1, 3, 41 * BLOCK), _edge_blocks()])
+    c, s = orc.quantize(x)
+    say("dequantize", x.size, "bf16" if bf16 else "f32")
+    out = torch.empty(x.size, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    lpc.lpc_dequantize_fp8(to_dev(c, dev), to_dev(s, dev), out)
+    assert_same(to_host(out), orc.dequantize(c, s, bf16=bf16), "dequantize")
+
+
+def test_zero_size_calls_are_noops(dev):
+    say("n == 0 no-ops")
+    e = torch.empty(0, device=dev)
+    lpc.lpc_quantize_fp8(e, torch.empty(0, dtype=torch.uint8, device=dev), torch.empty(0, device=dev))
+    lpc.dda_flat_reduce([torch.empty(0, dtype=torch.bfloat16, device=dev)] * 2,
+                        torch.empty(0, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+
+
+# -- low-precision allreduce ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_lp_allreduce_cfg1(dev, orc, fused):
+    N = inputs.CONFIGS[1]["nranks"]
+    xs = [inputs.rank_buffer(1, r) for r in range(N)]
+    say("lp allreduce cfg1 N=%d n=%d fused=%s" % (N, xs[0].size, fused))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, fused)
+    compare_allreduce(res, orc.lp_allreduce(xs), "cfg1")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 7, 8])
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_lp_allreduce_rank_counts(dev, orc, N, bf16):
+    """Every rank count 1..8 (one template instance each), ragged chunks (not a
+    multiple of the 4096-element workgroup tile), both dtypes."""
+    n = BLOCK * N * 37
+    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    if bf16:
+        xs = [inputs.truncate_to_bf16(x) for x in xs]
+    say("lp allreduce N=%d n=%d bf16=%s" % (N, n, bf16))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.bfloat16 if bf16 else torch.float32)
+    compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "N=%d" % N)
+
+
+def test_lp_allreduce_pages_example(dev):
+    """The Torchcomms quick-start on the pages: 10x20 tensors of the rank, SUM -> N(N-1)/2
+    everywhere (padded with zeros to whole blocks per chunk)."""
+    for N in (2, 4, 8):
+        say("pages example N=%d" % N)
+        xs = inputs.pages_example(N)
+        n = xs[0].size
+        unit = BLOCK * N
+        padded = -(-n // unit) * unit
+        bufs = [to_dev(np.concatenate([x.reshape(-1), np.zeros(padded - n, np.float32)]), dev) for x in xs]
+        res = gpu_lp_allreduce(bufs, torch.float32)
+        for out in res["outs"]:
+            assert torch.all(out[:n] == N * (N - 1) / 2)
+
+
+def test_lp_allreduce_cfg3_full(dev, orc):
+    """Workload 3 at full size (N=8, 16 MiB fp32 per rank, outliers), every intermediate."""
+    N = 8
+    xs = [inputs.rank_buffer(3, r) for r in range(N)]
+    say("lp allreduce cfg3 full N=8 n=%d" % xs[0].size)
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32)
+    compare_allreduce(res, orc.lp_allreduce(xs), "cfg3")
+
+
+def test_lp_allreduce_cfg4_sampled(dev, orc):
+    """Workload 4 at full size (N=8, 256 MiB bf16 per rank, Laplace): the whole path
+    on the GPU (fused kernel for ranks 0 and 7), checked on 96 sampled blocks per
+    chunk: every rank's codes and scales there, the reduced chunk, and the output."""
+    N = 8
+    n = inputs.CONFIGS[4]["n"]
+    C = n // N
+    say("lp allreduce cfg4 full-size N=8 n=%d (sampled check)" % n)
+    xs = [inputs.device_rank_buffer(4, r, dev) for r in range(N)]
+    q = [gpu_quantize(x) for x in xs]
+    codes = [c for c, _ in q]
+    scales = [s for _, s in q]
+    cc = [torch.empty(C, dtype=torch.uint8, device=dev) for _ in range(N)]
+    cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    for r in range(N):
+        lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
+    g = np.random.Generator(np.random.PCG64(107))
+    for r in (0, N - 1):
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        own_c = torch.empty(C, dtype=torch.uint8, device=dev)
+        own_s = torch.empty(C // BLOCK, dtype=torch.float32, device=dev)
+        lpc.lpc_rs_ag_fused(codes, scales, r, own_c, own_s, [None if p == r else cc[p] for p in range(N)],
+                            [None if p == r else cs[p] for p in range(N)], out)
+        torch.cuda.synchronize()
+        assert torch.equal(own_c, cc[r]) and torch.equal(own_s.view(torch.int32), cs[r].view(torch.int32))
+        for p in range(N):
+            blocks = np.sort(g.choice(C // BLOCK, size=96, replace=False))
+            blocks[0], blocks[-1] = 0, C // BLOCK - 1          # first and last block of the chunk
+            idx = torch.from_numpy(((p * C // BLOCK + blocks)[:, None] * BLOCK +
+                                    np.arange(BLOCK)[None, :]).reshape(-1)).to(dev)
+            xb = [to_host(x[idx]) for x in xs]                   # inputs of those blocks, every rank
+            for s_ in range(N):
+                rc, rs = orc.quantize(xb[s_], bf16=True)
+                assert_same(to_host(codes[s_][idx]), rc, "cfg4 codes rank %d" % s_)
+                assert_same(to_host(scales[s_][torch.from_numpy(p * C // BLOCK + blocks).to(dev)]), rs,
+                            "cfg4 scales rank %d" % s_)
+            # the sampled blocks form a little allreduce of their own (block-local arithmetic)
+            qb = [orc.quantize(x, bf16=True) for x in xb]
+            m = blocks.size * BLOCK
+            sum_codes, sum_scales = orc.reduce_scatter_chunk([np.tile(c, N) for c, _ in qb],
+                                                             [np.tile(s, N) for _, s in qb], 0)
+            assert sum_codes.size == m
+            lidx = torch.from_numpy((blocks[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)).to(dev)
+            assert_same(to_host(cc[p][lidx]), sum_codes, "cfg4 chunk codes %d" % p)
+            assert_same(to_host(cs[p][torch.from_numpy(blocks).to(dev)]), sum_scales, "cfg4 chunk scales %d" % p)
+            ref_out = orc.dequantize(sum_codes, sum_scales, bf16=True)
+            assert_same(to_host(out[idx]), ref_out, "cfg4 out rank %d chunk %d" % (r, p))
+        del out
+    del xs, codes, scales, cc, cs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_lp_reduce_scatter_one_quantization(dev, orc, bf16):
+    """Low-precision ReduceScatter: the FP32 rank-order sum of the owned chunk, unquantized."""
+    N = 8
+    n = BLOCK * N * 19
+    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    q = [orc.quantize(x) for x in xs]
+    codes = [to_dev(c, dev) for c, _ in q]
+    scales = [to_dev(s, dev) for _, s in q]
+    for r in (0, 3, N - 1):
+        say("lp reduce-scatter rank %d bf16=%s" % (r, bf16))
+        out = torch.empty(n // N, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+        lpc.lpc_reduce_scatter(codes, scales, r, out)
+        ref = orc.reduce_scatter_out([c for c, _ in q], [s for _, s in q], r, bf16=bf16)
+        assert_same(to_host(out), ref, "reduce_scatter rank %d" % r)
+
+
+# -- DDA ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tokens", inputs.DDA_TOKENS)
+def test_dda_flat_cfg2(dev, orc, tokens):
+    bufs = inputs.dda_buffers(tokens)
+    say("dda flat N=8 hidden 8192 x %d tokens" % tokens)
+    out = torch.empty(bufs[0].size, dtype=torch.bfloat16, device=dev)
+    lpc.dda_flat_reduce([to_dev(b, dev) for b in bufs], out)
+    assert_same(to_host(out), orc.dda_flat(bufs), "dda flat T=%d" % tokens)
+
+
+@pytest.mark.parametrize("N,n", [(1, 8), (2, 3), (3, 1001), (8, 8 * 977 + 5), (5, 4096 * 3 + 7)])
+def test_dda_flat_ragged(dev, orc, N, n):
+    bufs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(2, r), n, 0.5)) for r in range(N)]
+    say("dda flat ragged N=%d n=%d" % (N, n))
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    lpc.dda_flat_reduce([to_dev(b, dev) for b in bufs], out)
+    assert_same(to_host(out), orc.dda_flat(bufs), "dda flat ragged")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_dda_tree(dev, orc, bf16):
+    N, n = 8, 8 * 8 * 1001
+    fb = [inputs.normal_f32(inputs.rng(2, r), n, 0.5) for r in range(N)]
+    bufs = [inputs.truncate_to_bf16(x) for x in fb] if bf16 else fb
+    dt = torch.bfloat16 if bf16 else torch.float32
+    bd = [to_dev(b, dev) for b in bufs]
+    chunks = []
+    for r in range(N):
+        say("dda tree rs rank %d bf16=%s" % (r, bf16))
+        out = torch.empty(n // N, dtype=dt, device=dev)
+        lpc.dda_tree_reduce_scatter(bd, r, out)
+        assert_same(to_host(out), orc.dda_tree_rs(bufs, r, bf16), "dda tree rs %d" % r)
+        chunks.append(out)
+    full = torch.empty(n, dtype=dt, device=dev)
+    lpc.dda_tree_allgather(chunks, full)
+    assert_same(to_host(full), np.concatenate([to_host(c) for c in chunks]), "dda tree allgather")
+    if bf16:
+        assert_same(to_host(full), orc.dda_flat(bufs), "dda tree == dda flat")
+
+
+# -- all-to-all-v ----------------------------------------------------------------------------------
+
+def test_a2av_route_cfg5(dev, orc):
+    for rows, nranks in ((inputs.A2AV_ROWS, 8), (1, 8), (1000, 3), (70_000, 8)):
+        dest = inputs.zipf_destinations(rows=rows, nranks=nranks)
+        say("a2av route rows=%d nranks=%d" % (rows, nranks))
+        counts = torch.empty(nranks, dtype=torch.int32, device=dev)
+        offsets = torch.empty(nranks, dtype=torch.int32, device=dev)
+        perm = torch.empty(rows, dtype=torch.int32, device=dev)
+        lpc.lpc_a2av_route(to_dev(dest, dev), nranks, counts, offsets, perm)
+        rc, ro, rp = orc.a2av_route(dest, nranks)
+        assert_same(to_host(counts), rc, "counts")
+        assert_same(to_host(offsets), ro, "offsets")
+        assert_same(to_host(perm), rp, "perm")
+
+
+def test_a2av_route_drops_bad_destinations(dev):
+    dest = np.array([3, 9, 0, -1, 7, 0], np.int32)
+    say("a2av route with out-of-range destinations")
+    counts = torch.empty(8, dtype=torch.int32, device=dev)
+    offsets = torch.empty(8, dtype=torch.int32, device=dev)
+    perm = torch.empty(6, dtype=torch.int32, device=dev)
+    lpc.lpc_a2av_route(to_dev(dest, dev), 8, counts, offsets, perm)
+    assert to_host(counts).tolist() == [2, 0, 0, 1, 0, 0, 0, 1]
+    assert to_host(offsets).tolist() == [0, 2, 2, 2, 3, 3, 3, 3]
+    assert to_host(perm).tolist() == [2, 5, 0, 4, -1, -1]
+
+
+def test_a2av_quantize_rows_small(dev, orc):
+    rows, row_len = 300, inputs.A2AV_ROW_LEN
+    x = inputs.a2av_rows(rows, row_len)
+    _, _, perm = orc.a2av_route(inputs.zipf_destinations(rows=rows), 8)
+    perm_bad = perm.copy()
+    perm_bad[5] = -1
+    perm_bad[9] = rows
+    for name, p in (("routed", perm), ("with invalid entries", perm_bad)):
+        say("a2av quantize rows", name)
+        codes = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, row_len // BLOCK), dtype=torch.float32, device=dev)
+        lpc.lpc_quantize_fp8_rows(to_dev(x, dev), to_dev(p, dev), codes, scales)
+        if name == "routed":
+            rc, rs = orc.quantize_rows(x, p, bf16=True)
+        else:
+            rc, rs = orc.quantize_rows(x, perm, bf16=True)
+            for k in (5, 9):
+                rc[k] = 0
+                rs[k] = 0.0
+        assert_same(to_host(codes), rc, "rows codes")
+        assert_same(to_host(scales), rs, "rows scales")
+    # rows longer than 1024 granules take the multi-workgroup path
+    x2 = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(5, 1), 6 * 128 * 130, 1.0)).reshape(6, -1)
+    p2 = np.array([5, 0, 3, 1, 4, 2], np.int32)
+    say("a2av quantize long rows", x2.shape)
+    codes = torch.empty(x2.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty((6, x2.shape[1] // BLOCK), dtype=torch.float32, device=dev)
+    lpc.lpc_quantize_fp8_rows(to_dev(x2, dev), to_dev(p2, dev), codes, scales)
+    rc, rs = orc.quantize_rows(x2, p2, bf16=True)
+    assert_same(to_host(codes), rc, "long rows codes")
+    assert_same(to_host(scales), rs, "long rows scales")
+
+
+def test_a2av_cfg5_full_sampled(dev, orc):
+    """Workload 5 at full size: route, quantize + pack all 16,384 x 7168 rows, dequantize
+    the packed buffer; 192 packed rows checked against the oracle."""
+    rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
+    say("a2av cfg5 full rows=%d row_len=%d" % (rows, row_len))
+    x = inputs.a2av_rows()
+    dest = inputs.zipf_destinations()
+    xd, dd = to_dev(x, dev), to_dev(dest, dev)
+    counts = torch.empty(8, dtype=torch.int32, device=dev)
+    offsets = torch.empty(8, dtype=torch.int32, device=dev)
+    perm = torch.empty(rows, dtype=torch.int32, device=dev)
+    lpc.lpc_a2av_route(dd, 8, counts, offsets, perm)
+    codes = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, row_len // BLOCK), dtype=torch.float32, device=dev)
+    lpc.lpc_quantize_fp8_rows(xd, perm, codes, scales)
+    back = torch.empty((rows, row_len), dtype=torch.bfloat16, device=dev)
+    lpc.lpc_dequantize_fp8(codes, scales, back)
+    torch.cuda.synchronize()
+    rc, ro, rp = orc.a2av_route(dest, 8)
+    assert_same(to_host(perm), rp, "cfg5 perm")
+    assert int(to_host(counts).sum()) == rows
+    g = np.random.Generator(np.random.PCG64(109))
+    ks = np.concatenate([[0, rows - 1], ro, g.choice(rows, 180, replace=False)]).astype(np.int64)
+    for k in ks:
+        c, s = orc.quantize(x[rp[k]], bf16=True)
+        assert_same(to_host(codes[k]), c, "cfg5 packed row %d codes" % k)
+        assert_same(to_host(scales[k]), s, "cfg5 packed row %d scales" % k)
+        assert_same(to_host(back[k]), orc.dequantize(c, s, bf16=True), "cfg5 dequant row %d" % k)
