@@ -3,21 +3,40 @@
 
 Workload (the metric's configuration): N = 8 emulated ranks, 4,194,304 fp32
 elements (16 MiB) per rank, N(0,1) with 0.1% outliers x100, 128-element
-blocks.  One step is rank 0's share of the low-precision allreduce: quantize
-its buffer (lpc_quantize_fp8), then the fused reduce-scatter + all-gather
-(lpc_rs_ag_fused: reduce the owned chunk over all 8 ranks' FP8 buffers,
-requantize it, dequantize it and the 7 peers' requantized chunks into the
-output).  The other ranks' quantized buffers and reduced chunks are prepared
-untimed, as the peers would have produced them.
+blocks; plus the DDA-flat reduce of 8 x 64 KiB bf16 (hidden 8192 x 4 tokens).
 
-Inputs are resident in HBM when timing starts.  The step cycles through
-enough copies of every buffer (--sets) that the 256 MB Infinity Cache cannot
-hold them, so kernels stream from HBM; --sets 1 gives the cache-warm figure.
+One step is rank 0's share of the hot path on that workload:
+  1. lpc_quantize_fp8    quantize rank 0's 16 MiB buffer,
+  2. lpc_rs_ag_fused     reduce rank 0's chunk over all 8 ranks' FP8 buffers,
+                         requantize it, and dequantize it and the 7 peers'
+                         requantized chunks into the 16 MiB fp32 output,
+  3. dda_flat_reduce     8 x 64 KiB bf16 -> 64 KiB bf16.
+The other ranks' quantized buffers and reduced chunks are prepared untimed,
+as the peers would have produced them.  Inputs are resident in HBM when the
+timed region starts.
+
+Timing.  Every figure comes from HIP events on the stream the kernels run
+on.
+  * Per-kernel mean duration (value, roofline, kernels): a bounded spin
+    kernel is queued first, then the launches of one kernel back to back,
+    with one event before and one after them; the spin keeps the GPU behind
+    the host, so the launches run back to back on the GPU and the host's
+    launch cost stays out.  Mean = elapsed / launches (the pages' protocol:
+    warm-up, then the mean over the measured iterations).
+  * ms_per_step: one HIP graph of K steps, replayed once between two events.
+The timed launches cycle through enough buffer copies (--sets) that the
+256 MB Infinity Cache cannot hold them, so the kernels stream from HBM; the
+cache-warm DDA figure is reported beside the cold one.
 
 value = algorithmic bytes of one fused RS+AG launch / its mean duration
-(GB/s), durations from HIP events recorded around each launch on the stream
-the kernels run on.  The roofline object compares it with the 8 TB/s HBM
-peak.  DDA-flat latency (8 x 64 KiB bf16) is reported alongside.
+(GB/s).  roofline compares it with the 8 TB/s HBM peak; traffic is the HBM
+byte count per launch from rocprofv3 counters (profiles/traffic.json), null
+when those counters were taken on other kernel sources.  cpu_baseline is the
+CPU oracle on a bounded sample of the same share.
+
+Extra per-kernel lines (not part of the step): the unfused reduce-scatter
+and all-gather, the N=8 x 256 MiB bf16 fused launch, and the all-to-all-v
+row quantize and dequantize at 16,384 x 7168 bf16.
 """
 from __future__ import annotations
 
@@ -28,17 +47,35 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BLOCK = 128
+NRANKS = 8
+MALL_BYTES = 256 * 2 ** 20
+
+
+# -- algorithmic bytes (every byte read and written, scales included) -------------
+
+def chunk_bytes(C: int) -> int:
+    return C + C // BLOCK * 4                     # codes + scales of one chunk
 
 
 def fused_bytes(n: int, N: int, out_size: int) -> int:
     C = n // N
-    chunk = C + C // BLOCK * 4                   # codes + scales of one chunk
-    return N * chunk + chunk + (N - 1) * chunk + n * out_size
+    return N * chunk_bytes(C) + chunk_bytes(C) + (N - 1) * chunk_bytes(C) + n * out_size
+
+
+def rs_bytes(n: int, N: int) -> int:
+    C = n // N
+    return N * chunk_bytes(C) + chunk_bytes(C)
+
+
+def ag_bytes(n: int, N: int, out_size: int) -> int:
+    return N * chunk_bytes(n // N) + n * out_size
 
 
 def quantize_bytes(n: int, in_size: int) -> int:
@@ -104,15 +141,106 @@ def cpu_baseline(xs, min_seconds: float):
     }
 
 
+class GraphTimer:
+    """Capture `count` calls of fn(i) into one HIP graph on a side stream; time replays."""
+
+    def __init__(self, torch, fn, count: int):
+        self.torch = torch
+        self.count = count
+        self.stream = torch.cuda.Stream()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            fn(0)                       # one eager call on the capture stream before capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            for i in range(count):
+                fn(i)
+        torch.cuda.synchronize()
+
+    def replay_us(self, reps: int = 1) -> float:
+        """Mean device time per captured call over `reps` replays.  A replay runs on
+        the current stream, so the events are recorded there."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            self.graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * self.count)
+
+
+class BatchTimer:
+    """Mean device time per launch of a batch queued behind a spin kernel."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        torch.cuda._sleep(1000)                  # load the spin kernel before calibrating it
+        torch.cuda.synchronize()
+        cycles = 20_000_000
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)                  # the events bracket GPU work only
+        e0.record()
+        torch.cuda._sleep(cycles)
+        e1.record()
+        torch.cuda.synchronize()
+        self.cycles_per_us = cycles / max(e0.elapsed_time(e1) * 1e3, 1.0)
+
+    def run(self, fn, count: int):
+        """Launch fn(0..count-1) back to back; returns (mean us per launch, GPU was never idle)."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()                 # host cost per launch, from a short untimed batch
+        for i in range(min(count, 8)):
+            fn(i)
+        host_us = (time.perf_counter() - t0) * 1e6 / min(count, 8)
+        torch.cuda.synchronize()
+        spin_us = host_us * count * 2.0 + 1000.0
+        es = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        es.record()
+        torch.cuda._sleep(int(self.cycles_per_us * spin_us))
+        e0.record()
+        t1 = time.perf_counter()
+        for i in range(count):
+            fn(i)
+        enqueue_us = (time.perf_counter() - t1) * 1e6
+        e1.record()
+        torch.cuda.synchronize()
+        # the spin started no later than the host began enqueueing; it must outlast the enqueueing
+        fed = es.elapsed_time(e0) * 1e3 > enqueue_us
+        return e0.elapsed_time(e1) * 1e3 / count, fed
+
+
+def stats(res, count, nbytes=None):
+    us, fed = res
+    d = {"us": round(us, 3), "launches": count, "gpu_fed": bool(fed)}
+    if nbytes:
+        d["bytes"] = nbytes
+        d["gbps"] = round(nbytes / us / 1e3, 1)
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sets", type=int, default=16, help="buffer copies cycled through (1 = cache-warm)")
+    ap.add_argument("--sets", type=int, default=16, help="buffer copies of the 16 MiB workload cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--dda-steps", type=int, default=200)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-kernel lines outside the step (256 MiB bf16, all-to-all-v)")
+    ap.add_argument("--dda-sets", type=int, default=0,
+                    help="DDA buffer sets cycled through (0: enough to exceed the 256 MB cache)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 64 MiB device copy (calibration for counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -120,22 +248,23 @@ def main():
               "in one GPU's HBM); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from fp8_precision_allreduce_amd import inputs, lpc
 
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
     lpc.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-    N = 8
+    N = NRANKS
     n = inputs.CONFIGS[3]["n"]
     C = n // N
-    print("[bench] generating workload: N=%d x %d fp32 per rank" % (N, n), file=sys.stderr, flush=True)
+    log("generating workload: N=%d x %d fp32 per rank" % (N, n))
     xs_host = [inputs.rank_buffer(3, r) for r in range(N)]
 
-    # -- untimed setup: every rank's quantized buffer and reduced chunk -------------
+    # -- untimed setup: every rank's quantized buffer and reduced chunk ------------------
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
     codes = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(N)]
     scales = [torch.empty(n // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
@@ -145,9 +274,10 @@ def main():
     cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
     for r in range(N):
         lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
+    out_ref = torch.empty(n, dtype=torch.float32, device=dev)
+    lpc.lpc_allgather_dequant(cc, cs, out_ref)
     torch.cuda.synchronize()
 
-    # -- buffer sets cycled through by the timed steps -----------------------------------
     S = max(1, args.sets)
     sets = []
     for _ in range(S):
@@ -157,100 +287,202 @@ def main():
             scales=[s.clone() for s in scales],
             peer_c=[None] + [c.clone() for c in cc[1:]],
             peer_s=[None] + [s.clone() for s in cs[1:]],
+            all_c=[c.clone() for c in cc],
+            all_s=[s.clone() for s in cs],
             own_c=torch.empty(C, dtype=torch.uint8, device=dev),
             own_s=torch.empty(C // BLOCK, dtype=torch.float32, device=dev),
             out=torch.empty(n, dtype=torch.float32, device=dev),
         ))
+    set_bytes = sum(t.numel() * t.element_size() for b in sets[:1] for k, v in b.items()
+                    for t in (v if isinstance(v, list) else [v]) if t is not None)
+
+    # DDA flat sets: 8 ranks x (hidden 8192 x T) bf16 + output, enough to exceed the cache
+    dda_host = {T: inputs.dda_buffers(T) for T in inputs.DDA_TOKENS}
+
+    def dda_sets(T, count):
+        m = dda_host[T][0].size
+        pool = torch.empty((count, N + 1, m), dtype=torch.bfloat16, device=dev)
+        src = torch.stack([torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[T]])
+        pool[:, :N].copy_(src.unsqueeze(0).expand(count, N, m))
+        return pool
+
+    def dda_cold_count(T):
+        if args.dda_sets > 0:
+            return args.dda_sets
+        m = dda_host[T][0].size
+        return max(64, -(-2 * MALL_BYTES // dda_bytes(m, N)))
+
+    pools = {T: dda_sets(T, dda_cold_count(T)) for T in inputs.DDA_TOKENS}
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    # -- the kernels --------------------------------------------------------------------------
+    def quantize(i):
         b = sets[i % S]
-        if ev is not None:
-            ev[0].record(stream)
-        lpc.lpc_quantize_fp8(b["x"], b["codes"][0], b["scales"][0], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["own_c"], b["own_s"], b["peer_c"], b["peer_s"],
-                            b["out"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        lpc.lpc_quantize_fp8(b["x"], b["codes"][0], b["scales"][0])
 
+    def fused(i):
+        b = sets[i % S]
+        lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["own_c"], b["own_s"], b["peer_c"], b["peer_s"],
+                            b["out"])
+
+    def rs_chunk(i):
+        b = sets[i % S]
+        lpc.lpc_reduce_scatter_chunk(b["codes"], b["scales"], 0, b["own_c"], b["own_s"])
+
+    def allgather(i):
+        b = sets[i % S]
+        lpc.lpc_allgather_dequant(b["all_c"], b["all_s"], b["out"])
+
+    def dda(T, i):
+        pool = pools[T]
+        k = i % pool.shape[0]
+        lpc.dda_flat_reduce([pool[k, p] for p in range(N)], pool[k, N])
+
+    def step(i):
+        quantize(i)
+        fused(i)
+        dda(4, i)
+
+    # -- warmup (eager), then graph capture of the K steps -------------------------------------------
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # -- timed region: K steps, events around each launch ------------------------------------
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        step(args.warmup + i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    f_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    log("capturing graphs (%d steps)" % K)
+    g_step = GraphTimer(torch, step, K)
+    g_step.replay_us(1)                     # warm replay, untimed
 
-    # correctness spot check of the last step against the untimed reference chunk
-    last = sets[(args.warmup + K - 1) % S]
-    assert torch.equal(last["own_c"], cc[0]), "fused kernel's reduced chunk changed between runs"
+    # -- timed region: exactly K steps ------------------------------------------------------------------
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    step_us = g_step.replay_us(1)
+    wall_s = time.perf_counter() - t_wall
+    total_ms = step_us * K / 1e3
+
+    # -- per-kernel mean durations, each batch after a cache-evicting replay ------------------------------
+    timer = BatchTimer(torch)
+    L = max(K, 2 * S)
+
+    def timed(fn, count, nbytes=None):
+        g_step.replay_us(1)                 # >1 GB of other traffic: the batch starts cache-cold
+        return stats(timer.run(fn, count), count, nbytes)
 
     fb = fused_bytes(n, N, 4)
-    qb = quantize_bytes(n, 4)
-    f_mean_s = float(f_ms.mean()) * 1e-3
-    q_mean_s = float(q_ms.mean()) * 1e-3
-    value = fb / f_mean_s / 1e9
-
-    # -- back-to-back launches (no events between): loop-average duration ---------------------
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(K):
-        b = sets[i % S]
-        lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["own_c"], b["own_s"], b["peer_c"], b["peer_s"],
-                            b["out"], stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    f_loop_us = e0.elapsed_time(e1) / K * 1e3
-
-    # -- DDA flat, 8 ranks x 64 KiB bf16 (hidden 8192 x 4 tokens) ------------------------------
-    dda = {}
+    kernels = {
+        "rs_ag_fused_f32_16MiB": timed(fused, L, fb),
+        "quantize_f32_16MiB": timed(quantize, L, quantize_bytes(n, 4)),
+        "reduce_scatter_chunk_16MiB": timed(rs_chunk, L, rs_bytes(n, N)),
+        "allgather_dequant_f32_16MiB": timed(allgather, L, ag_bytes(n, N, 4)),
+    }
+    dda_res = {}
     for T in inputs.DDA_TOKENS:
-        bufs_h = inputs.dda_buffers(T)
-        m = bufs_h[0].size
-        DS = max(1, min(S * 8, 64))
-        dsets = [([torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in bufs_h],
-                  torch.empty(m, dtype=torch.bfloat16, device=dev)) for _ in range(DS)]
-        for i in range(20):
-            lpc.dda_flat_reduce(dsets[i % DS][0], dsets[i % DS][1], stream=stream)
+        m = dda_host[T][0].size
+        cnt = min(K, pools[T].shape[0])
+        r = timed(lambda i, T=T: dda(T, i), cnt, dda_bytes(m, N))
+        r["buffer_sets"] = cnt
+        dda_res["%dKiB" % (m * 2 // 1024)] = r
+    warm = stats(timer.run(lambda i: dda(4, i % 4), K), K)
+    dda_res["64KiB"]["us_warm"] = warm["us"]
+
+    # -- the same two headline kernels as graph replays (back to back inside one graph) --------------------
+    g_fused = GraphTimer(torch, fused, L)
+    g_dda = GraphTimer(torch, lambda i: dda(4, i), pools[4].shape[0])
+    g_fused.replay_us(1)
+    g_dda.replay_us(1)
+    kernels["rs_ag_fused_f32_16MiB"]["graph_replay_us"] = round(g_fused.replay_us(3), 3)
+    dda_res["64KiB"]["graph_replay_us"] = round(g_dda.replay_us(3), 3)
+
+    # -- every launch and replay left the eager result in place --------------------------------------------
+    for b in sets:
+        assert torch.equal(b["own_c"], cc[0]), "reduced chunk differs from the eager result"
+        assert torch.equal(b["own_s"].view(torch.int32), cs[0].view(torch.int32)), "chunk scales differ"
+        assert torch.equal(b["out"].view(torch.int32), out_ref.view(torch.int32)), "output differs"
+        assert torch.equal(b["codes"][0], codes[0]), "quantized buffer differs"
+    for T in inputs.DDA_TOKENS:
+        pool = pools[T]
+        ref = torch.empty_like(pool[0, N])
+        lpc.dda_flat_reduce([pool[0, p] for p in range(N)], ref)
+        written = pool[:min(K, pool.shape[0]), N]
+        assert torch.equal(written.view(torch.int16), ref.view(torch.int16).expand_as(written)), \
+            "DDA flat output differs"
+    torch.cuda.synchronize()
+
+    f_us = kernels["rs_ag_fused_f32_16MiB"]["us"]
+    value = fb / (f_us * 1e-6) / 1e9
+    del g_step, g_fused, g_dda, pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # -- extra per-kernel lines: 256 MiB bf16 per rank, all-to-all-v rows ------------------------------
+    if not args.no_extra:
+        log("256 MiB bf16 per rank (device-generated) and all-to-all-v rows")
+        n4 = inputs.CONFIGS[4]["n"]
+        C4 = n4 // N
+        codes4 = []
+        scales4 = []
+        for r in range(N):
+            x4 = inputs.device_rank_buffer(4, r, dev)
+            codes4.append(torch.empty(n4, dtype=torch.uint8, device=dev))
+            scales4.append(torch.empty(n4 // BLOCK, dtype=torch.float32, device=dev))
+            lpc.lpc_quantize_fp8(x4, codes4[-1], scales4[-1])
+            if r == 0:
+                x4_0 = x4
+            else:
+                del x4
+        cc4 = [torch.empty(C4, dtype=torch.uint8, device=dev) for _ in range(N)]
+        cs4 = [torch.empty(C4 // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+        for r in range(N):
+            lpc.lpc_reduce_scatter_chunk(codes4, scales4, r, cc4[r], cs4[r])
+        out4 = torch.empty(n4, dtype=torch.bfloat16, device=dev)
+        oc4 = torch.empty(C4, dtype=torch.uint8, device=dev)
+        os4 = torch.empty(C4 // BLOCK, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
-        D = args.dda_steps
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(D)]
-        for i in range(D):
-            bset, o = dsets[i % DS]
-            dev_ev[i][0].record(stream)
-            lpc.dda_flat_reduce(bset, o, stream=stream)
-            dev_ev[i][1].record(stream)
+        for i in range(3):
+            lpc.lpc_rs_ag_fused(codes4, scales4, 0, oc4, os4, [None] + cc4[1:], [None] + cs4[1:], out4)
+            lpc.lpc_quantize_fp8(x4_0, codes4[0], scales4[0])
         torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) for a, b in dev_ev]) * 1e3
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for i in range(D):
-            bset, o = dsets[i % DS]
-            lpc.dda_flat_reduce(bset, o, stream=stream)
-        a1.record(stream)
+        kernels["rs_ag_fused_bf16_256MiB"] = stats(timer.run(
+            lambda i: lpc.lpc_rs_ag_fused(codes4, scales4, 0, oc4, os4, [None] + cc4[1:], [None] + cs4[1:], out4),
+            20), 20, fused_bytes(n4, N, 2))
+        kernels["quantize_bf16_256MiB"] = stats(timer.run(
+            lambda i: lpc.lpc_quantize_fp8(x4_0, codes4[0], scales4[0]), 20), 20, quantize_bytes(n4, 2))
+        assert torch.equal(oc4, cc4[0]), "256 MiB bf16: reduced chunk differs"
+        del codes4, scales4, cc4, cs4, out4, oc4, os4, x4_0
         torch.cuda.synchronize()
-        dda["%dKiB" % (m * 2 // 1024)] = {
-            "event_us_mean": round(float(us.mean()), 3),
-            "event_us_median": round(float(np.median(us)), 3),
-            "loop_us_per_call": round(a0.elapsed_time(a1) / D * 1e3, 3),
-            "bytes": dda_bytes(m, 8),
-        }
-        del dsets
+        torch.cuda.empty_cache()
+
+        rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
+        xr = torch.from_numpy(inputs.a2av_rows().view(np.int16)).to(dev).view(torch.bfloat16)
+        dest = torch.from_numpy(inputs.zipf_destinations()).to(dev)
+        counts = torch.empty(N, dtype=torch.int32, device=dev)
+        offsets = torch.empty(N, dtype=torch.int32, device=dev)
+        perm = torch.empty(rows, dtype=torch.int32, device=dev)
+        rc = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
+        rsc = torch.empty((rows, row_len // BLOCK), dtype=torch.float32, device=dev)
+        back = torch.empty((rows, row_len), dtype=torch.bfloat16, device=dev)
+        lpc.lpc_a2av_route(dest, N, counts, offsets, perm)
+        torch.cuda.synchronize()
+        lpc.lpc_quantize_fp8_rows(xr, perm, rc, rsc)
+        lpc.lpc_dequantize_fp8(rc, rsc, back)
+        torch.cuda.synchronize()
+        m5 = rows * row_len
+        kernels["a2av_route_16384"] = stats(timer.run(
+            lambda i: lpc.lpc_a2av_route(dest, N, counts, offsets, perm), 20), 20, rows * 4 * 2 + N * 8)
+        kernels["a2av_quantize_rows_bf16"] = stats(timer.run(
+            lambda i: lpc.lpc_quantize_fp8_rows(xr, perm, rc, rsc), 20), 20, quantize_bytes(m5, 2) + rows * 4)
+        kernels["a2av_dequantize_bf16"] = stats(timer.run(
+            lambda i: lpc.lpc_dequantize_fp8(rc, rsc, back), 20), 20, m5 + m5 // BLOCK * 4 + m5 * 2)
+        del xr, rc, rsc, back
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    if args.copy_probe:
+        # a plain copy of known size (64 MiB read, 64 MiB written): the DDA-tree gather copy
+        src = [torch.ones(2 * 2 ** 20, dtype=torch.float32, device=dev) for _ in range(N)]
+        dst = torch.empty(16 * 2 ** 20, dtype=torch.float32, device=dev)
+        for _ in range(5):
+            lpc.dda_tree_allgather(src, dst)
+        torch.cuda.synchronize()
 
     traffic = traffic_from_profiles("rs_ag_fused_kernel<8,float>")
     result = {
@@ -265,12 +497,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3/f32",
-        "data": "synthetic (seeded N(0,1) fp32 with 0.1% outliers x100)",
+        "data": "synthetic (seeded N(0,1) fp32 with 0.1% outliers x100; DDA: seeded N(0,0.5) bf16)",
         "config": {
-            "workload": "lp_allreduce_n8_16MiB_f32: one rank's share of an N=8 FP8 low-precision "
-                        "allreduce, 4,194,304 fp32 per rank, 128-element blocks, E4M3 + FP32 scales",
-            "nranks": N, "elems_per_rank": n, "block": BLOCK, "step": "quantize + fused RS+AG",
-            "buffer_sets": S, "hbm_resident": True,
+            "workload": "lp_allreduce_n8_16MiB_f32 + dda_flat_n8_64KiB_bf16: rank 0's share of an N=8 FP8 "
+                        "low-precision allreduce, 4,194,304 fp32 per rank, 128-element blocks, E4M3 + FP32 "
+                        "scales; DDA-flat reduce of 8 x 32,768 bf16",
+            "nranks": N, "elems_per_rank": n, "block": BLOCK,
+            "step": "quantize + fused RS+AG + DDA flat 64 KiB",
+            "buffer_sets": S, "set_bytes": set_bytes, "hbm_resident": True,
+            "timing": "kernels: back-to-back batch behind a spin kernel, HIP events around it; step: HIP graph replay",
         },
         "roofline": {
             "bound": "hbm",
@@ -281,24 +516,17 @@ def main():
             "traffic": traffic,
             "kernel": "rs_ag_fused_kernel<8,float>",
             "bytes_per_launch": fb,
-            "mean_us": round(f_mean_s * 1e6, 3),
+            "mean_us": round(f_us, 3),
+            "launches": kernels["rs_ag_fused_f32_16MiB"]["launches"],
         },
-        "kernels": {
-            "rs_ag_fused": {"event_us_mean": round(float(f_ms.mean()) * 1e3, 3),
-                            "event_us_median": round(float(np.median(f_ms)) * 1e3, 3),
-                            "event_us_min": round(float(f_ms.min()) * 1e3, 3),
-                            "loop_us_per_launch": round(f_loop_us, 3),
-                            "bytes": fb, "gbps": round(value, 2)},
-            "quantize_f32": {"event_us_mean": round(q_mean_s * 1e6, 3),
-                             "event_us_median": round(float(np.median(q_ms)) * 1e3, 3),
-                             "bytes": qb, "gbps": round(qb / q_mean_s / 1e9, 2)},
-        },
-        "dda_flat_n8_bf16": dda,
-        "dda_flat_us_64KiB": dda.get("64KiB", {}).get("event_us_mean"),
+        "kernels": kernels,
+        "dda_flat_n8_bf16": dda_res,
+        "dda_flat_us_64KiB": dda_res["64KiB"]["us"],
+        "step_wall_s": round(wall_s, 6),
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(xs_host, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None

@@ -1,16 +1,25 @@
 // lpc_device.hpp -- device-side building blocks for the gfx950 FP8 codec kernels.
 //
-// Element layout shared by every kernel: one lane owns a "granule" of 16
-// contiguous elements, so the 8 adjacent lanes of a wavefront-aligned group
-// own one 128-element scale block.  A lane moves its granule with 16-byte
-// vector loads/stores (fp32: 4, bf16: 2, codes: 1) and the block's absmax is
-// reduced across its 8 lanes with DPP moves inside the wavefront (no LDS).
+// Two element layouts are used:
+//   * granule (quantize): one lane owns 16 contiguous elements, so the 8
+//     adjacent lanes of a wavefront-aligned group own one 128-element scale
+//     block; the block absmax is reduced across those 8 lanes with DPP.
+//   * quad (reduce-scatter, all-gather, dequantize): one lane owns 4
+//     contiguous elements, so a wavefront's loads and stores are single
+//     contiguous runs (256 codes, 1 KiB of fp32) and 32 lanes own a block;
+//     the absmax is reduced with DPP inside each 16-lane row and one
+//     ds_swizzle between the two rows of the half-wavefront.
+// No kernel allocates LDS for these reductions.
 //
 // FP8 is OCP E4M3FN (the gfx950 native FP8 format): the conversions below use
 // the gfx950 instructions v_cvt_pk_fp8_f32 (round to nearest even) and
 // v_cvt_pk_f32_fp8 (exact).  Values are clamped to +-448 first with v_med3,
 // which makes the conversion saturating whatever the instruction does on
 // overflow.
+//
+// Large outputs are written with non-temporal stores: they are not read again
+// by the kernel, and streaming them past the L2 leaves no dirty lines for the
+// end-of-kernel write-back.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,8 +30,10 @@
 namespace lpc {
 
 constexpr int kBlock = 128;        // elements per scale
-constexpr int kGranule = 16;       // elements per lane
+constexpr int kGranule = 16;       // elements per lane (granule layout)
 constexpr int kLanesPerBlock = kBlock / kGranule;  // 8
+constexpr int kQuad = 4;           // elements per lane (quad layout)
+constexpr int kLanesPerBlockQ = kBlock / kQuad;    // 32
 constexpr float kFp8Max = 448.0f;
 constexpr int kMaxRanks = 8;
 
@@ -49,6 +60,36 @@ __device__ __forceinline__ float group8_max(float v) {
     x = __float_as_int(v);
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)));
     return v;
+}
+
+// Max over the 32-lane half-wavefront of a block in the quad layout:
+// group8_max, then row_mirror (lane i <-> 15-i: joins the two 8-lane halves
+// of a row), then ds_swizzle in bit mode with xor mask 16 (swaps the two
+// 16-lane rows of each 32-lane group).
+__device__ __forceinline__ float group32_max(float v) {
+    v = group8_max(v);
+    int x = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    constexpr int kSwapRows = 0x1F | (0x10 << 10);  // and_mask 0x1F, or_mask 0, xor_mask 0x10
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(x, kSwapRows)));
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware tile order
+// ---------------------------------------------------------------------------
+
+// Workgroups of a launch are handed to the 8 XCDs round-robin by workgroup
+// id.  This maps blockIdx.x to a tile index so that each XCD gets one
+// contiguous run of tiles: neighbouring tiles share scale cache lines, and
+// this way they share them inside one XCD's L2.  A bijection on
+// [0, gridDim.x) for any grid size.
+__device__ __forceinline__ size_t xcd_tile() {
+    constexpr unsigned kXcds = 8;
+    const unsigned nwg = gridDim.x, b = blockIdx.x;
+    const unsigned per = nwg / kXcds, rem = nwg % kXcds;
+    const unsigned x = b % kXcds, k = b / kXcds;
+    return (size_t)(x * per + (x < rem ? x : rem) + k);
 }
 
 // ---------------------------------------------------------------------------
@@ -94,6 +135,24 @@ __device__ __forceinline__ void dequant16(uint4 c, float s, float (&d)[kGranule]
     decode4(c.w, d + 12);
 #pragma unroll
     for (int j = 0; j < kGranule; ++j) d[j] = d[j] * s;
+}
+
+// d[j] = fl32(E4M3(code byte j) * s) for the four codes of a dword
+__device__ __forceinline__ void dequant4(uint32_t c, float s, float (&d)[kQuad]) {
+    decode4(c, d);
+#pragma unroll
+    for (int j = 0; j < kQuad; ++j) d[j] = d[j] * s;
+}
+
+// Blockwise quantization of a quad whose 32-lane group forms one block:
+// returns the four codes and sets *scale (identical in all 32 lanes).
+__device__ __forceinline__ uint32_t quantize_quad(const float (&v)[kQuad], float* scale) {
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = group32_max(amax);
+    const float s = amax / kFp8Max;
+    *scale = s;
+    if (s == 0.0f) return 0u;
+    return encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
 }
 
 // Blockwise quantization of a granule whose 8-lane group forms one block:
@@ -152,6 +211,24 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&v
             v[8 * j + 2 * k + 1] = bf16hi(w[k]);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// quad stores (non-temporal)
+// ---------------------------------------------------------------------------
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_quad_nt(float* __restrict__ p, const float (&d)[kQuad]) {
+    const f32x4_t v = {d[0], d[1], d[2], d[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
+__device__ __forceinline__ void store_quad_nt(uint16_t* __restrict__ p, const float (&d)[kQuad]) {
+    const u32x2_t v = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
 __device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[kGranule]) {

@@ -2,10 +2,12 @@
 // and their launchers.  Arguments reaching these launchers have been checked
 // by the C ABI layer (lpc_api.hip); nothing here validates again.
 //
-// All streaming kernels use 256-lane workgroups and one 16-element granule
-// per lane (see lpc_device.hpp), so a wavefront covers 8 scale blocks and a
-// workgroup 4096 elements.  Rank loops are unrolled by template parameter so
-// that all N loads of a lane are in flight before the first add.
+// The quantizers use one 16-element granule per lane (a wavefront covers 8
+// scale blocks); the reduce-scatter, all-gather, fused and dequantize kernels
+// use one 4-element quad per lane (a wavefront covers 2 blocks), see
+// lpc_device.hpp.  Streaming kernels use 256-lane workgroups.  Rank loops are
+// unrolled by template parameter so that all N loads of a lane are in flight
+// before the first add.
 #include "lpc_device.hpp"
 #include "lpc_launch.hpp"
 
@@ -22,6 +24,12 @@ __device__ __forceinline__ size_t granule_id() {
     return (size_t)blockIdx.x * kThreads + threadIdx.x;
 }
 
+// Every kernel of the library is launched through this helper.
+template <typename K, typename... Args>
+static void launch(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream, Args... args) {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+}
+
 // ---------------------------------------------------------------------------
 // (1) quantize
 // ---------------------------------------------------------------------------
@@ -36,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict
     load16(x + g * kGranule, v);
     float s;
     const uint4 c = quantize_granule(v, &s);
-    *reinterpret_cast<uint4*>(codes + g * kGranule) = c;
+    const u32x4_t cv = {c.x, c.y, c.z, c.w};
+    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + g * kGranule));
     if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
 }
 
@@ -44,71 +53,86 @@ hipError_t launch_quantize(const void* x, int in_bf16, size_t n, uint8_t* codes,
                            hipStream_t stream) {
     const size_t ngran = n / kGranule;
     if (in_bf16)
-        hipLaunchKernelGGL(quantize_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream,
+        launch(quantize_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(x), ngran, codes, scales);
     else
-        hipLaunchKernelGGL(quantize_kernel<float>, grid_for(ngran), dim3(kThreads), 0, stream,
+        launch(quantize_kernel<float>, grid_for(ngran), dim3(kThreads), 0, stream,
                            static_cast<const float*>(x), ngran, codes, scales);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// (2) reduce-scatter step: N-way dequant + rank-order FP32 sum of one chunk
+// Quad-layout kernels: one lane owns 4 contiguous elements of a chunk, 32
+// lanes a scale block; tiles are taken in XCD-aware order.
 // ---------------------------------------------------------------------------
 
-// Sum of the granule at element offset `e` (rank-buffer index) over N ranks.
+static inline dim3 quad_grid(size_t elems, unsigned y = 1) {
+    const size_t lanes = elems / kQuad;
+    return dim3((unsigned)((lanes + kThreads - 1) / kThreads), y, 1);
+}
+
+__device__ __forceinline__ size_t quad_elem() {
+    return (xcd_tile() * kThreads + threadIdx.x) * kQuad;
+}
+
+// Rank-order FP32 sum of the quad at rank-buffer offset e over N ranks: all
+// N code and scale loads are issued before the first add.
 template <int N>
-__device__ __forceinline__ void rank_sum16(const RankCodes& in, size_t e, float (&acc)[kGranule]) {
-    uint4 c[N];
+__device__ __forceinline__ void rank_sum4(const RankCodes& in, size_t e, float (&acc)[kQuad]) {
+    uint32_t c[N];
     float s[N];
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-        c[p] = *reinterpret_cast<const uint4*>(in.codes[p] + e);
+        c[p] = *reinterpret_cast<const uint32_t*>(in.codes[p] + e);
         s[p] = in.scales[p][e / kBlock];
     }
-    dequant16(c[0], s[0], acc);
+    dequant4(c[0], s[0], acc);
 #pragma unroll
     for (int p = 1; p < N; ++p) {
-        float d[kGranule];
-        dequant16(c[p], s[p], d);
+        float d[kQuad];
+        dequant4(c[p], s[p], d);
 #pragma unroll
-        for (int j = 0; j < kGranule; ++j) acc[j] = acc[j] + d[j];
+        for (int j = 0; j < kQuad; ++j) acc[j] = acc[j] + d[j];
     }
 }
+
+// ---------------------------------------------------------------------------
+// (2) reduce-scatter step: N-way dequant + rank-order FP32 sum of one chunk,
+// requantized (kRequant) or written out as the sum (kSumF32 / kSumBF16).
+// ---------------------------------------------------------------------------
 
 enum RsOut { kRequant = 0, kSumF32 = 1, kSumBF16 = 2 };
 
 template <int N, int Mode>
-__global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RankCodes in, size_t chunk_off,
-                                                                  size_t cgran,
+__global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RankCodes in, size_t chunk_off, size_t C,
                                                                   uint8_t* __restrict__ cc,
                                                                   float* __restrict__ cs,
                                                                   void* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= cgran) return;
-    float acc[kGranule];
-    rank_sum16<N>(in, chunk_off + g * kGranule, acc);
+    const size_t i = quad_elem();
+    if (i >= C) return;  // whole 32-lane blocks drop out together (C % 128 == 0)
+    float acc[kQuad];
+    rank_sum4<N>(in, chunk_off + i, acc);
     if (Mode == kRequant) {
         float s;
-        const uint4 c = quantize_granule(acc, &s);
-        *reinterpret_cast<uint4*>(cc + g * kGranule) = c;
-        if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) cs[g / kLanesPerBlock] = s;
+        const uint32_t c = quantize_quad(acc, &s);
+        *reinterpret_cast<uint32_t*>(cc + i) = c;
+        if ((threadIdx.x & (kLanesPerBlockQ - 1)) == 0) cs[i / kBlock] = s;
     } else if (Mode == kSumF32) {
-        store16(static_cast<float*>(out) + g * kGranule, acc);
+        store_quad_nt(static_cast<float*>(out) + i, acc);
     } else {
-        store16(static_cast<uint16_t*>(out) + g * kGranule, acc);
+        store_quad_nt(static_cast<uint16_t*>(out) + i, acc);
     }
 }
 
 template <int Mode>
-static void launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_t cgran, uint8_t* cc,
-                        float* cs, void* out, hipStream_t stream) {
-    const dim3 grid = grid_for(cgran), block(kThreads);
+static void launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_t C, uint8_t* cc, float* cs,
+                        void* out, hipStream_t stream) {
+    const dim3 grid = quad_grid(C), block(kThreads);
     switch (nranks) {
 #define LPC_RS_CASE(NR)                                                                              \
     case NR:                                                                                         \
-        hipLaunchKernelGGL((reduce_scatter_kernel<NR, Mode>), grid, block, 0, stream, in, chunk_off, \
-                           cgran, cc, cs, out);                                                      \
+        launch((reduce_scatter_kernel<NR, Mode>), grid, block, 0, stream, in, chunk_off, \
+                           C, cc, cs, out);                                                          \
         break;
         LPC_RS_CASE(1) LPC_RS_CASE(2) LPC_RS_CASE(3) LPC_RS_CASE(4)
         LPC_RS_CASE(5) LPC_RS_CASE(6) LPC_RS_CASE(7) LPC_RS_CASE(8)
@@ -119,7 +143,7 @@ static void launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_
 hipError_t launch_reduce_scatter_chunk(const RankCodes& in, int nranks, int rank, size_t n,
                                        uint8_t* cc, float* cs, hipStream_t stream) {
     const size_t C = n / nranks;
-    launch_rs_n<kRequant>(in, nranks, (size_t)rank * C, C / kGranule, cc, cs, nullptr, stream);
+    launch_rs_n<kRequant>(in, nranks, (size_t)rank * C, C, cc, cs, nullptr, stream);
     return hipGetLastError();
 }
 
@@ -127,119 +151,157 @@ hipError_t launch_reduce_scatter_out(const RankCodes& in, int nranks, int rank, 
                                      int out_bf16, hipStream_t stream) {
     const size_t C = n / nranks;
     if (out_bf16)
-        launch_rs_n<kSumBF16>(in, nranks, (size_t)rank * C, C / kGranule, nullptr, nullptr, out, stream);
+        launch_rs_n<kSumBF16>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
     else
-        launch_rs_n<kSumF32>(in, nranks, (size_t)rank * C, C / kGranule, nullptr, nullptr, out, stream);
+        launch_rs_n<kSumF32>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// (3) all-gather dequantization;  flat dequantization
+// (3) all-gather dequantization (grid.y = chunk);  flat dequantization
 // ---------------------------------------------------------------------------
 
 template <typename Out>
-__device__ __forceinline__ void dequant_granule_to(const uint8_t* __restrict__ codes,
-                                                   const float* __restrict__ scales, size_t g,
-                                                   Out* __restrict__ out) {
-    const uint4 c = *reinterpret_cast<const uint4*>(codes + g * kGranule);
-    const float s = scales[g / kLanesPerBlock];
-    float d[kGranule];
-    dequant16(c, s, d);
-    store16(out + g * kGranule, d);
-}
-
-// grid.y = chunk p; out chunk p at p*C
-template <typename Out>
-__global__ __launch_bounds__(kThreads) void allgather_kernel(RankCodes chunks, size_t cgran,
+__global__ __launch_bounds__(kThreads) void allgather_kernel(RankCodes chunks, size_t C,
                                                              Out* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= cgran) return;
+    const size_t i = quad_elem();
+    if (i >= C) return;
     const int p = blockIdx.y;
-    dequant_granule_to(chunks.codes[p], chunks.scales[p], g, out + (size_t)p * cgran * kGranule);
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(chunks.codes[p] + i);
+    float d[kQuad];
+    dequant4(c, chunks.scales[p][i / kBlock], d);
+    store_quad_nt(out + (size_t)p * C + i, d);
 }
 
 hipError_t launch_allgather(const RankCodes& chunks, int nranks, size_t n, void* out, int out_bf16,
                             hipStream_t stream) {
-    const size_t cgran = n / nranks / kGranule;
+    const size_t C = n / nranks;
     if (out_bf16)
-        hipLaunchKernelGGL(allgather_kernel<uint16_t>, grid_for(cgran, nranks), dim3(kThreads), 0,
-                           stream, chunks, cgran, static_cast<uint16_t*>(out));
+        launch(allgather_kernel<uint16_t>, quad_grid(C, nranks), dim3(kThreads), 0, stream,
+                           chunks, C, static_cast<uint16_t*>(out));
     else
-        hipLaunchKernelGGL(allgather_kernel<float>, grid_for(cgran, nranks), dim3(kThreads), 0,
-                           stream, chunks, cgran, static_cast<float*>(out));
+        launch(allgather_kernel<float>, quad_grid(C, nranks), dim3(kThreads), 0, stream,
+                           chunks, C, static_cast<float*>(out));
     return hipGetLastError();
 }
 
 template <typename Out>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
-                                                           const float* __restrict__ scales,
-                                                           size_t ngran, Out* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= ngran) return;
-    dequant_granule_to(codes, scales, g, out);
+                                                           const float* __restrict__ scales, size_t n,
+                                                           Out* __restrict__ out) {
+    const size_t i = quad_elem();
+    if (i >= n) return;
+    float d[kQuad];
+    dequant4(*reinterpret_cast<const uint32_t*>(codes + i), scales[i / kBlock], d);
+    store_quad_nt(out + i, d);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, void* out, int out_bf16,
                           hipStream_t stream) {
-    const size_t ngran = n / kGranule;
     if (out_bf16)
-        hipLaunchKernelGGL(dequant_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream, codes,
-                           scales, ngran, static_cast<uint16_t*>(out));
+        launch(dequant_kernel<uint16_t>, quad_grid(n), dim3(kThreads), 0, stream, codes, scales,
+                           n, static_cast<uint16_t*>(out));
     else
-        hipLaunchKernelGGL(dequant_kernel<float>, grid_for(ngran), dim3(kThreads), 0, stream, codes,
-                           scales, ngran, static_cast<float*>(out));
+        launch(dequant_kernel<float>, quad_grid(n), dim3(kThreads), 0, stream, codes, scales,
+                           n, static_cast<float*>(out));
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// (2)+(3) fused: grid.y == 0 reduces and requantizes the own chunk and writes
-// its dequantization from registers; grid.y = q > 0 dequantizes peer chunk
-// (rank + q) % N.  The own-chunk row is dispatched first.
+// (2)+(3) fused.  Every lane owns the same quad position i of every chunk.
+// The peers' chunks are split into slices of two (peer q = rank + 1 ..
+// rank + N - 1, mod N): grid.y == 0 reduces and requantizes the own chunk at
+// i, writes its dequantization from registers, and dequantizes peers q = 1, 2
+// at i; grid.y == y > 0 dequantizes peers q = 2y + 1, 2y + 2.  Each lane issues
+// all of its loads before its first conversion.
 // ---------------------------------------------------------------------------
+
+constexpr int kPeersPerSlice = 2;
+
+__host__ __device__ constexpr int fused_slices(int N) {
+    return N <= 1 ? 1 : (N - 1 + kPeersPerSlice - 1) / kPeersPerSlice;
+}
 
 template <int N, typename Out>
 __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, RankCodes peers, int rank,
-                                                               size_t cgran, uint8_t* __restrict__ cc,
+                                                               size_t C, uint8_t* __restrict__ cc,
                                                                float* __restrict__ cs,
                                                                Out* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= cgran) return;
-    const size_t C = cgran * kGranule;
-    float d[kGranule];
-    size_t out_off;
-    if (blockIdx.y == 0) {
-        const size_t chunk_off = (size_t)rank * C;
-        float acc[kGranule];
-        rank_sum16<N>(in, chunk_off + g * kGranule, acc);
-        float s;
-        const uint4 c = quantize_granule(acc, &s);
-        *reinterpret_cast<uint4*>(cc + g * kGranule) = c;
-        if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) cs[g / kLanesPerBlock] = s;
-        dequant16(c, s, d);  // own chunk straight from registers
-        out_off = chunk_off + g * kGranule;
-    } else {
-        int p = rank + (int)blockIdx.y;
+    const size_t i = quad_elem();
+    if (i >= C) return;
+    const int y = blockIdx.y;
+    const int q_first = kPeersPerSlice * y + 1;
+    uint32_t pc[kPeersPerSlice];
+    float ps[kPeersPerSlice];
+    int pp[kPeersPerSlice];
+#pragma unroll
+    for (int k = 0; k < kPeersPerSlice; ++k) {
+        int p = rank + q_first + k;
         if (p >= N) p -= N;
-        const uint4 c = *reinterpret_cast<const uint4*>(peers.codes[p] + g * kGranule);
-        dequant16(c, peers.scales[p][g / kLanesPerBlock], d);
-        out_off = (size_t)p * C + g * kGranule;
+        pp[k] = p;
     }
-    store16(out + out_off, d);
+    float d[kQuad];
+    if (y == 0) {
+        const size_t own = (size_t)rank * C + i;
+        uint32_t c[N];
+        float s[N];
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            c[p] = *reinterpret_cast<const uint32_t*>(in.codes[p] + own);
+            s[p] = in.scales[p][own / kBlock];
+        }
+#pragma unroll
+        for (int k = 0; k < kPeersPerSlice; ++k) {
+            if (q_first + k < N) {
+                pc[k] = *reinterpret_cast<const uint32_t*>(peers.codes[pp[k]] + i);
+                ps[k] = peers.scales[pp[k]][i / kBlock];
+            }
+        }
+        float acc[kQuad];
+        dequant4(c[0], s[0], acc);
+#pragma unroll
+        for (int p = 1; p < N; ++p) {
+            dequant4(c[p], s[p], d);
+#pragma unroll
+            for (int j = 0; j < kQuad; ++j) acc[j] = acc[j] + d[j];
+        }
+        float sc;
+        const uint32_t code = quantize_quad(acc, &sc);
+        *reinterpret_cast<uint32_t*>(cc + i) = code;
+        if ((threadIdx.x & (kLanesPerBlockQ - 1)) == 0) cs[i / kBlock] = sc;
+        dequant4(code, sc, d);  // own chunk straight from registers
+        store_quad_nt(out + own, d);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPeersPerSlice; ++k) {
+            if (q_first + k < N) {
+                pc[k] = *reinterpret_cast<const uint32_t*>(peers.codes[pp[k]] + i);
+                ps[k] = peers.scales[pp[k]][i / kBlock];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPeersPerSlice; ++k) {
+        if (q_first + k < N) {
+            dequant4(pc[k], ps[k], d);
+            store_quad_nt(out + (size_t)pp[k] * C + i, d);
+        }
+    }
 }
 
 hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int nranks, int rank, size_t n,
                               uint8_t* cc, float* cs, void* out, int out_bf16, hipStream_t stream) {
-    const size_t cgran = n / nranks / kGranule;
-    const dim3 grid = grid_for(cgran, nranks), block(kThreads);
+    const size_t C = n / nranks;
+    const dim3 block(kThreads);
     switch (nranks) {
-#define LPC_FUSED_CASE(NR)                                                                           \
-    case NR:                                                                                         \
-        if (out_bf16)                                                                                \
-            hipLaunchKernelGGL((rs_ag_fused_kernel<NR, uint16_t>), grid, block, 0, stream, in, peers, \
-                               rank, cgran, cc, cs, static_cast<uint16_t*>(out));                    \
-        else                                                                                         \
-            hipLaunchKernelGGL((rs_ag_fused_kernel<NR, float>), grid, block, 0, stream, in, peers,    \
-                               rank, cgran, cc, cs, static_cast<float*>(out));                       \
+#define LPC_FUSED_CASE(NR)                                                                               \
+    case NR:                                                                                             \
+        if (out_bf16)                                                                                    \
+            launch((rs_ag_fused_kernel<NR, uint16_t>), quad_grid(C, fused_slices(NR)), block, \
+                               0, stream, in, peers, rank, C, cc, cs, static_cast<uint16_t*>(out));      \
+        else                                                                                             \
+            launch((rs_ag_fused_kernel<NR, float>), quad_grid(C, fused_slices(NR)), block,   \
+                               0, stream, in, peers, rank, C, cc, cs, static_cast<float*>(out));         \
         break;
         LPC_FUSED_CASE(1) LPC_FUSED_CASE(2) LPC_FUSED_CASE(3) LPC_FUSED_CASE(4)
         LPC_FUSED_CASE(5) LPC_FUSED_CASE(6) LPC_FUSED_CASE(7) LPC_FUSED_CASE(8)
@@ -249,42 +311,33 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
 }
 
 // ---------------------------------------------------------------------------
-// DDA flat: N bf16 buffers -> FP32 rank-order sum -> bf16.  One lane owns 8
-// bf16 (one 16-byte load per rank); the last partial granule goes element by
-// element.
+// DDA flat: N bf16 buffers -> FP32 rank-order sum -> bf16.  Small messages
+// are latency-bound, so the launch spreads them thin: one lane owns 4 bf16
+// (one 8-byte load per rank), 64-lane workgroups; the last partial quad goes
+// element by element.
 // ---------------------------------------------------------------------------
 
+constexpr int kDdaThreads = 64;
+constexpr int kDdaElems = 4;
+
 template <int N>
-__global__ __launch_bounds__(kThreads) void dda_flat_kernel(RankBufs b, size_t n,
-                                                            uint16_t* __restrict__ out) {
-    const size_t g = granule_id();
-    const size_t e = g * 8;
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t n,
+                                                               uint16_t* __restrict__ out) {
+    const size_t e = ((size_t)blockIdx.x * kDdaThreads + threadIdx.x) * kDdaElems;
     if (e >= n) return;
-    if (e + 8 <= n) {
-        uint4 v[N];
+    if (e + kDdaElems <= n) {
+        uint2 v[N];
 #pragma unroll
-        for (int p = 0; p < N; ++p) v[p] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(b.p[p]) + e);
-        float acc[8];
-        {
-            const uint32_t w[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc[2 * k] = bf16lo(w[k]);
-                acc[2 * k + 1] = bf16hi(w[k]);
-            }
-        }
+        for (int p = 0; p < N; ++p) v[p] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(b.p[p]) + e);
+        float acc[kDdaElems] = {bf16lo(v[0].x), bf16hi(v[0].x), bf16lo(v[0].y), bf16hi(v[0].y)};
 #pragma unroll
         for (int p = 1; p < N; ++p) {
-            const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc[2 * k] = acc[2 * k] + bf16lo(w[k]);
-                acc[2 * k + 1] = acc[2 * k + 1] + bf16hi(w[k]);
-            }
+            acc[0] = acc[0] + bf16lo(v[p].x);
+            acc[1] = acc[1] + bf16hi(v[p].x);
+            acc[2] = acc[2] + bf16lo(v[p].y);
+            acc[3] = acc[3] + bf16hi(v[p].y);
         }
-        *reinterpret_cast<uint4*>(out + e) =
-            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                       pack_bf16x2(acc[6], acc[7]));
+        *reinterpret_cast<uint2*>(out + e) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     } else {
         for (size_t i = e; i < n; ++i) {
             float acc = __uint_as_float((uint32_t)static_cast<const uint16_t*>(b.p[0])[i] << 16);
@@ -298,13 +351,13 @@ __global__ __launch_bounds__(kThreads) void dda_flat_kernel(RankBufs b, size_t n
 }
 
 hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, hipStream_t stream) {
-    const size_t ngran = (n + 7) / 8;
-    const dim3 grid = grid_for(ngran), block(kThreads);
+    const size_t lanes = (n + kDdaElems - 1) / kDdaElems;
+    const dim3 grid((unsigned)((lanes + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
     uint16_t* o = static_cast<uint16_t*>(out);
     switch (nranks) {
 #define LPC_DDA_CASE(NR)                                                                 \
     case NR:                                                                             \
-        hipLaunchKernelGGL((dda_flat_kernel<NR>), grid, block, 0, stream, b, n, o);      \
+        launch((dda_flat_kernel<NR>), grid, block, 0, stream, b, n, o);      \
         break;
         LPC_DDA_CASE(1) LPC_DDA_CASE(2) LPC_DDA_CASE(3) LPC_DDA_CASE(4)
         LPC_DDA_CASE(5) LPC_DDA_CASE(6) LPC_DDA_CASE(7) LPC_DDA_CASE(8)
@@ -372,9 +425,9 @@ hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank,
 #define LPC_TREE_CASE(NR)                                                                              \
     case NR:                                                                                           \
         if (bf16)                                                                                      \
-            hipLaunchKernelGGL((dda_tree_rs_kernel<NR, true>), grid, block, 0, stream, b, off, ngran, out); \
+            launch((dda_tree_rs_kernel<NR, true>), grid, block, 0, stream, b, off, ngran, out); \
         else                                                                                           \
-            hipLaunchKernelGGL((dda_tree_rs_kernel<NR, false>), grid, block, 0, stream, b, off, ngran, out); \
+            launch((dda_tree_rs_kernel<NR, false>), grid, block, 0, stream, b, off, ngran, out); \
         break;
         LPC_TREE_CASE(1) LPC_TREE_CASE(2) LPC_TREE_CASE(3) LPC_TREE_CASE(4)
         LPC_TREE_CASE(5) LPC_TREE_CASE(6) LPC_TREE_CASE(7) LPC_TREE_CASE(8)
@@ -388,14 +441,15 @@ __global__ __launch_bounds__(kThreads) void gather_copy_kernel(RankBufs chunks, 
     const size_t g = granule_id();
     if (g >= ngran) return;
     const int p = blockIdx.y;
-    out[(size_t)p * ngran + g] = reinterpret_cast<const uint4*>(chunks.p[p])[g];
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(chunks.p[p])[g];
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out) + (size_t)p * ngran + g);
 }
 
 hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size_t n, void* out,
                               hipStream_t stream) {
     const size_t esz = bf16 ? 2 : 4;
     const size_t ngran = n / nranks * esz / 16;
-    hipLaunchKernelGGL(gather_copy_kernel, grid_for(ngran, nranks), dim3(kThreads), 0, stream, chunks,
+    launch(gather_copy_kernel, grid_for(ngran, nranks), dim3(kThreads), 0, stream, chunks,
                        ngran, static_cast<uint4*>(out));
     return hipGetLastError();
 }
@@ -494,7 +548,7 @@ __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t
 
 hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32_t* counts, int32_t* offsets,
                              int32_t* perm, hipStream_t stream) {
-    hipLaunchKernelGGL(a2av_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, dest, rows, nranks, counts,
+    launch(a2av_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, dest, rows, nranks, counts,
                        offsets, perm);
     return hipGetLastError();
 }
@@ -543,10 +597,10 @@ hipError_t launch_quantize_rows(const void* x, int in_bf16, size_t rows, size_t 
     const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
     const dim3 grid(gx, gy, 1), block(threads);
     if (in_bf16)
-        hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x),
+        launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x),
                            rows, row_len, perm, codes, scales);
     else
-        hipLaunchKernelGGL(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows,
+        launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows,
                            row_len, perm, codes, scales);
     return hipGetLastError();
 }
@@ -571,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 
 hipError_t launch_encode(const float* x, size_t n, uint8_t* codes, hipStream_t stream) {
     const size_t ngran = (n + 3) / 4;
-    hipLaunchKernelGGL(encode_kernel, grid_for(ngran), dim3(kThreads), 0, stream, x, n, codes);
+    launch(encode_kernel, grid_for(ngran), dim3(kThreads), 0, stream, x, n, codes);
     return hipGetLastError();
 }
 

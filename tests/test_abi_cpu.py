@@ -169,3 +169,4 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lpc, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         lpc.lib()
+

@@ -232,18 +232,81 @@ def test_lp_allreduce_cfg1(dev, orc, fused):
     compare_allreduce(res, orc.lp_allreduce(xs), "cfg1")
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 5, 7, 8])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_lp_allreduce_rank_counts(dev, orc, N, bf16):
-    """Every rank count 1..8 (one template instance each), ragged chunks (not a
-    multiple of the 4096-element workgroup tile), both dtypes."""
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_lp_allreduce_rank_counts(dev, orc, N, bf16, fused):
+    """Every rank count 1..8 (one template instance each), ragged chunks (an odd
+    number of blocks, so the last wavefront is half empty, and a workgroup count
+    that is not a multiple of the 8 XCDs), both dtypes, fused and unfused."""
     n = BLOCK * N * 37
     xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
     if bf16:
         xs = [inputs.truncate_to_bf16(x) for x in xs]
-    say("lp allreduce N=%d n=%d bf16=%s" % (N, n, bf16))
-    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.bfloat16 if bf16 else torch.float32)
+    say("lp allreduce N=%d n=%d bf16=%s fused=%s" % (N, n, bf16, fused))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.bfloat16 if bf16 else torch.float32, fused)
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "N=%d" % N)
+
+
+@pytest.mark.parametrize("chunk_blocks", [1, 2, 7, 8, 9, 63, 64, 65, 8 * 64 + 3])
+def test_fused_chunk_sizes(dev, orc, chunk_blocks):
+    """Chunk sizes around the wavefront (2 blocks), workgroup (8 blocks) and XCD
+    (8 workgroups) granularities: every tile of the XCD-aware order is visited
+    exactly once."""
+    N = 8
+    n = BLOCK * N * chunk_blocks
+    xs = [inputs.rank_buffer(1, r, n) for r in range(N)]
+    say("fused chunk of %d blocks, N=8" % chunk_blocks)
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, True)
+    compare_allreduce(res, orc.lp_allreduce(xs), "chunk_blocks=%d" % chunk_blocks)
+
+
+def test_graph_replays_match_eager(dev):
+    """The benchmark times HIP graph replays: capture quantize + fused RS+AG + DDA
+    flat, replay it three times with eager work and synchronisation in between,
+    and check every replay against the eager result."""
+    N = 8
+    n = BLOCK * N * 40
+    C = n // N
+    xs = [to_dev(inputs.rank_buffer(3, r, n), dev) for r in range(N)]
+    q = [gpu_quantize(x) for x in xs]
+    codes = [c for c, _ in q]
+    scales = [s for _, s in q]
+    cc = [torch.empty(C, dtype=torch.uint8, device=dev) for _ in range(N)]
+    cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    for r in range(N):
+        lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
+    bufs = [to_dev(b, dev) for b in inputs.dda_buffers(1)]
+    own_c = torch.empty(C, dtype=torch.uint8, device=dev)
+    own_s = torch.empty(C // BLOCK, dtype=torch.float32, device=dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    dout = torch.empty_like(bufs[0])
+    q0c = torch.empty(n, dtype=torch.uint8, device=dev)
+    q0s = torch.empty(n // BLOCK, dtype=torch.float32, device=dev)
+
+    def step():
+        lpc.lpc_quantize_fp8(xs[0], q0c, q0s)
+        lpc.lpc_rs_ag_fused(codes, scales, 0, own_c, own_s, [None] + cc[1:], [None] + cs[1:], out)
+        lpc.dda_flat_reduce(bufs, dout)
+
+    say("graph replay vs eager")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (q0c, q0s, own_c, own_s, out, dout)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (q0c, q0s, own_c, own_s, out, dout):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((q0c, q0s, own_c, own_s, out, dout), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep
 
 
 def test_lp_allreduce_pages_example(dev):
