@@ -35,8 +35,10 @@ when those counters were taken on other kernel sources.  cpu_baseline is the
 CPU oracle on a bounded sample of the same share.
 
 Extra per-kernel lines (not part of the step): the unfused reduce-scatter
-and all-gather, the N=8 x 256 MiB bf16 fused launch, and the all-to-all-v
-row quantize and dequantize at 16,384 x 7168 bf16.
+and all-gather, the one-quantization low-precision reduce-scatter, the DDA
+tree phases at 2 MiB bf16 per rank, the full emulated 8-rank allreduce
+(low precision and DDA tree), the N=8 x 256 MiB bf16 fused launch, and the
+all-to-all-v route, row quantize and dequantize at 16,384 x 7168 bf16.
 """
 from __future__ import annotations
 
@@ -86,10 +88,14 @@ def dda_bytes(n: int, N: int) -> int:
     return (N + 1) * n * 2
 
 
+KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every kernel's device code lives in these two
+
+
 def source_digest() -> str:
+    """Digest of the kernels' device sources (the counters in profiles/ are valid for it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_precision_allreduce_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -406,6 +412,36 @@ def main():
         assert torch.equal(written.view(torch.int16), ref.view(torch.int16).expand_as(written)), \
             "DDA flat output differs"
     torch.cuda.synchronize()
+
+    # -- next rows: one-quantization reduce-scatter, DDA tree, the emulated 8-rank allreduce ---------------
+    def lp_rs(i):
+        b = sets[i % S]
+        lpc.lpc_reduce_scatter(b["codes"], b["scales"], 0, b["rs_out"])
+
+    for b in sets:
+        b["rs_out"] = torch.empty(C, dtype=torch.float32, device=dev)
+    kernels["lp_reduce_scatter_f32_16MiB"] = timed(lp_rs, L, N * chunk_bytes(C) + C * 4)
+    nt = 8 * 2 ** 20 // 16 * 2                            # 2 MiB of bf16 per rank
+    tree_sets = [[torch.randn(nt, device=dev).to(torch.bfloat16) for _ in range(N)] for _ in range(S)]
+    tree_chunks = [[torch.empty(nt // N, dtype=torch.bfloat16, device=dev) for _ in range(N)] for _ in range(S)]
+    tree_out = [torch.empty(nt, dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    kernels["dda_tree_rs_bf16_2MiB"] = timed(
+        lambda i: lpc.dda_tree_reduce_scatter(tree_sets[i % S], 0, tree_chunks[i % S][0]), L,
+        N * (nt // N) * 2 + (nt // N) * 2)
+    kernels["dda_tree_ag_bf16_2MiB"] = timed(
+        lambda i: lpc.dda_tree_allgather(tree_chunks[i % S], tree_out[i % S]), L, nt * 2 * 2)
+    for algo, name, dt in ((lpc.ALGO_LOW_PRECISION, "low_precision", torch.float32),
+                           (lpc.ALGO_DDA_TREE, "dda_tree", torch.float32)):
+        ar_bufs = [[b["out"]] + [torch.empty(n, dtype=dt, device=dev) for _ in range(N - 1)] for b in sets[:4]]
+        for bl in ar_bufs:
+            for t in bl:
+                t.copy_(xs[0])
+        ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, n, dt), dtype=torch.uint8, device=dev)
+        r = stats(timer.run(lambda i: lpc.lpc_allreduce_emulated(ar_bufs[i % 4], algo, ws), 8), 8)
+        r["what"] = "all 8 ranks' shares, one after another, in place"
+        kernels["allreduce_emulated_%s_n8_16MiB" % name] = r
+        del ar_bufs, ws
+    del tree_sets, tree_chunks, tree_out
 
     f_us = kernels["rs_ag_fused_f32_16MiB"]["us"]
     value = fb / (f_us * 1e-6) / 1e9

@@ -1,0 +1,161 @@
+// lpc_allreduce.hip -- allreduce over emulated ranks on one GPU, and the
+// size-based algorithm choice (the extern "C" calls of include/lpc.h's
+// "Allreduce over emulated ranks" section).
+//
+// Nothing here computes: an emulated allreduce enqueues, rank after rank, the
+// same per-rank entry points a real rank would call, with the other ranks'
+// buffers standing in for its peers' memory.  All arguments are checked
+// before the first call, so a validation error enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lpc.h"
+
+namespace {
+
+constexpr size_t kRegionAlign = 256;  // every workspace region starts on a 256-byte boundary
+
+size_t align_up(size_t x) { return (x + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
+
+bool bad_dtype(lpc_dtype t) { return t != LPC_F32 && t != LPC_BF16; }
+
+size_t elem_bytes(lpc_dtype t) { return t == LPC_BF16 ? 2 : 4; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Workspace regions of the low-precision algorithm, in bytes from the start.
+struct LpLayout {
+    size_t codes[LPC_MAX_RANKS], scales[LPC_MAX_RANKS];   // every rank's quantized buffer
+    size_t ccodes[LPC_MAX_RANKS], cscales[LPC_MAX_RANKS]; // every rank's requantized chunk
+    size_t total;
+};
+
+LpLayout lp_layout(int nranks, size_t n) {
+    LpLayout L{};
+    const size_t C = n / (size_t)nranks;
+    size_t off = 0;
+    for (int r = 0; r < nranks; ++r) {
+        L.codes[r] = off;
+        off += align_up(n);
+        L.scales[r] = off;
+        off += align_up(n / LPC_BLOCK * sizeof(float));
+    }
+    for (int r = 0; r < nranks; ++r) {
+        L.ccodes[r] = off;
+        off += align_up(C);
+        L.cscales[r] = off;
+        off += align_up(C / LPC_BLOCK * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+// Argument checks shared by the workspace query and the allreduce itself.
+lpc_status check_args(lpc_algo algo, int nranks, size_t n, lpc_dtype t) {
+    if (bad_dtype(t)) return LPC_ERR_DTYPE;
+    if (algo != LPC_ALGO_DDA_FLAT && algo != LPC_ALGO_DDA_TREE && algo != LPC_ALGO_LOW_PRECISION)
+        return LPC_ERR_DTYPE;
+    if (algo == LPC_ALGO_DDA_FLAT && t != LPC_BF16) return LPC_ERR_DTYPE;
+    if (nranks < 1 || nranks > LPC_MAX_RANKS) return LPC_ERR_RANKS;
+    if (n > LPC_MAX_ELEMS) return LPC_ERR_SHAPE;
+    if (algo == LPC_ALGO_DDA_TREE && n % ((size_t)8 * nranks)) return LPC_ERR_SHAPE;
+    if (algo == LPC_ALGO_LOW_PRECISION && n % ((size_t)LPC_BLOCK * nranks)) return LPC_ERR_SHAPE;
+    return LPC_OK;
+}
+
+size_t workspace_bytes(lpc_algo algo, int nranks, size_t n, lpc_dtype t) {
+    switch (algo) {
+        case LPC_ALGO_DDA_FLAT: return (size_t)nranks * align_up(n * 2);
+        case LPC_ALGO_DDA_TREE: return (size_t)nranks * align_up(n / (size_t)nranks * elem_bytes(t));
+        case LPC_ALGO_LOW_PRECISION: return lp_layout(nranks, n).total;
+        default: return 0;
+    }
+}
+
+#define LPC_TRY(expr)                        \
+    do {                                     \
+        const lpc_status st_ = (expr);       \
+        if (st_ != LPC_OK) return st_;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+lpc_algo lpc_select_algo(int nranks, size_t n, lpc_dtype t, int low_precision_enabled) {
+    if (bad_dtype(t) || nranks < 1 || nranks > LPC_MAX_RANKS || n > LPC_MAX_ELEMS) return LPC_ALGO_AUTO;
+    const size_t bytes = n * elem_bytes(t);
+    if (t == LPC_BF16 && bytes <= LPC_DDA_FLAT_MAX_BYTES) return LPC_ALGO_DDA_FLAT;
+    if (low_precision_enabled && bytes >= LPC_LOW_PRECISION_MIN_BYTES && n % ((size_t)LPC_BLOCK * nranks) == 0)
+        return LPC_ALGO_LOW_PRECISION;
+    if (n % ((size_t)8 * nranks) == 0) return LPC_ALGO_DDA_TREE;
+    if (t == LPC_BF16) return LPC_ALGO_DDA_FLAT;
+    return LPC_ALGO_AUTO;
+}
+
+lpc_status lpc_allreduce_workspace_bytes(lpc_algo algo, int nranks, size_t n, lpc_dtype t, size_t* bytes) {
+    LPC_TRY(check_args(algo, nranks, n, t));
+    if (!bytes) return LPC_ERR_NULL;
+    *bytes = workspace_bytes(algo, nranks, n, t);
+    return LPC_OK;
+}
+
+lpc_status lpc_allreduce_emulated(void* const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+    LPC_TRY(check_args(algo, nranks, n, t));
+    if (n == 0) return LPC_OK;
+    if (!bufs || !workspace) return LPC_ERR_NULL;
+    for (int r = 0; r < nranks; ++r)
+        if (!bufs[r]) return LPC_ERR_NULL;
+    for (int r = 0; r < nranks; ++r)
+        if (misaligned(bufs[r])) return LPC_ERR_ALIGN;
+    if (misaligned(workspace)) return LPC_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(algo, nranks, n, t)) return LPC_ERR_SHAPE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const void* in[LPC_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) in[r] = bufs[r];
+
+    if (algo == LPC_ALGO_DDA_FLAT) {
+        // every rank reduces all buffers into its own output, then takes it in place
+        const size_t slot = align_up(n * 2);
+        for (int r = 0; r < nranks; ++r) LPC_TRY(dda_flat_reduce(in, nranks, n, ws + r * slot, stream));
+        for (int r = 0; r < nranks; ++r)
+            if (hipMemcpyAsync(bufs[r], ws + r * slot, n * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+                return LPC_ERR_HIP;
+        return LPC_OK;
+    }
+    if (algo == LPC_ALGO_DDA_TREE) {
+        const size_t slot = align_up(n / (size_t)nranks * elem_bytes(t));
+        const void* chunks[LPC_MAX_RANKS];
+        for (int r = 0; r < nranks; ++r) {
+            chunks[r] = ws + r * slot;
+            LPC_TRY(dda_tree_reduce_scatter(in, t, nranks, r, n, ws + r * slot, stream));
+        }
+        for (int r = 0; r < nranks; ++r) LPC_TRY(dda_tree_allgather(chunks, t, nranks, n, bufs[r], stream));
+        return LPC_OK;
+    }
+    // low precision: quantize every rank, reduce-scatter every chunk, all-gather into every buffer
+    const LpLayout L = lp_layout(nranks, n);
+    const uint8_t* codes[LPC_MAX_RANKS];
+    const float* scales[LPC_MAX_RANKS];
+    const uint8_t* ccodes[LPC_MAX_RANKS];
+    const float* cscales[LPC_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) {
+        codes[r] = ws + L.codes[r];
+        scales[r] = reinterpret_cast<const float*>(ws + L.scales[r]);
+        ccodes[r] = ws + L.ccodes[r];
+        cscales[r] = reinterpret_cast<const float*>(ws + L.cscales[r]);
+    }
+    for (int r = 0; r < nranks; ++r)
+        LPC_TRY(lpc_quantize_fp8(bufs[r], t, n, ws + L.codes[r], reinterpret_cast<float*>(ws + L.scales[r]),
+                                 stream));
+    for (int r = 0; r < nranks; ++r)
+        LPC_TRY(lpc_reduce_scatter_chunk(codes, scales, nranks, r, n, ws + L.ccodes[r],
+                                         reinterpret_cast<float*>(ws + L.cscales[r]), stream));
+    for (int r = 0; r < nranks; ++r)
+        LPC_TRY(lpc_allgather_dequant(ccodes, cscales, nranks, n, bufs[r], t, stream));
+    return LPC_OK;
+}
+
+}  // extern "C"

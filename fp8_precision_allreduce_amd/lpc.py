@@ -25,6 +25,9 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lpc.h")
 BLOCK = 128
 MAX_RANKS = 8
 LPC_F32, LPC_BF16 = 0, 1
+ALGO_AUTO, ALGO_DDA_FLAT, ALGO_DDA_TREE, ALGO_LOW_PRECISION = 0, 1, 2, 3
+ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DDA_FLAT: "dda_flat", ALGO_DDA_TREE: "dda_tree",
+              ALGO_LOW_PRECISION: "low_precision"}
 STATUS = ["LPC_OK", "LPC_ERR_NULL", "LPC_ERR_SHAPE", "LPC_ERR_RANKS", "LPC_ERR_DTYPE",
           "LPC_ERR_ALIGN", "LPC_ERR_HIP"]
 
@@ -51,6 +54,9 @@ SIGNATURES = {
     "lpc_quantize_fp8_rows": [_vp, _int, _sz, _sz, _vp, _vp, _vp, _vp],
     "lpc_dequantize_fp8": [_vp, _vp, _sz, _vp, _int, _vp],
     "lpc_e4m3_encode": [_vp, _sz, _vp, _vp],
+    "lpc_select_algo": [_int, _sz, _int, _int],
+    "lpc_allreduce_workspace_bytes": [_int, _int, _sz, _int, ctypes.POINTER(ctypes.c_size_t)],
+    "lpc_allreduce_emulated": [_pp, _int, _sz, _int, _int, _vp, _sz, _vp],
 }
 
 _lock = threading.Lock()
@@ -238,6 +244,28 @@ def lpc_dequantize_fp8(codes, scales, out: torch.Tensor, stream=None):
     n = out.numel()
     _call("lpc_dequantize_fp8", _dev(codes, "codes", _U8, n), _dev(scales, "scales", _F32, n // BLOCK),
           n, _dev(out, "out", _FB), _dtype(out), _stream(stream))
+
+
+def lpc_select_algo(nranks: int, n: int, dtype, low_precision_enabled: bool) -> int:
+    """Algorithm the library picks for an allreduce of n elements per rank (no GPU call)."""
+    t = LPC_BF16 if dtype == torch.bfloat16 else LPC_F32 if dtype == torch.float32 else 99
+    return lib().lpc_select_algo(nranks, n, t, 1 if low_precision_enabled else 0)
+
+
+def lpc_allreduce_workspace_bytes(algo: int, nranks: int, n: int, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    t = LPC_BF16 if dtype == torch.bfloat16 else LPC_F32 if dtype == torch.float32 else 99
+    _call("lpc_allreduce_workspace_bytes", algo, nranks, n, t, ctypes.byref(out))
+    return out.value
+
+
+def lpc_allreduce_emulated(bufs, algo: int, workspace: torch.Tensor, stream=None):
+    """In-place allreduce (SUM) of the N rank buffers `bufs` (same shape and dtype)."""
+    N = len(bufs)
+    n = bufs[0].numel()
+    dt = bufs[0].dtype
+    _call("lpc_allreduce_emulated", _ptrs(bufs, "bufs", (dt,), n), N, n, _dtype(bufs[0]), algo,
+          _dev(workspace, "workspace", _U8), workspace.numel(), _stream(stream))
 
 
 def lpc_e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None):

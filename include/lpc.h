@@ -211,6 +211,68 @@ lpc_status lpc_dequantize_fp8(const uint8_t *codes, const float *scales, size_t 
                               void *out, lpc_dtype out_t, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Allreduce over emulated ranks, with algorithm selection                  */
+/* ---------------------------------------------------------------------- */
+
+/* Allreduce algorithms of the pages (infolabhq pages, Direct Data Access and
+ * low-precision sections; RCCLX post, DDA and low-precision sections): DDA
+ * flat for small messages, DDA tree (reduce-scatter + all-gather with direct
+ * access) for slightly larger ones, low-precision FP8 for large messages when
+ * enabled (the pages switch it on with an environment variable).          */
+typedef enum {
+    LPC_ALGO_AUTO = 0,           /* choose with lpc_select_algo */
+    LPC_ALGO_DDA_FLAT = 1,       /* bf16 only */
+    LPC_ALGO_DDA_TREE = 2,
+    LPC_ALGO_LOW_PRECISION = 3
+} lpc_algo;
+
+/* Size thresholds of lpc_select_algo, in bytes per rank.  The pages give the
+ * ordering (flat < tree < low precision) and the 16 MB floor of the
+ * low-precision collectives, not the flat/tree boundary. */
+#define LPC_DDA_FLAT_MAX_BYTES ((size_t)512 << 10)
+#define LPC_LOW_PRECISION_MIN_BYTES ((size_t)16 << 20)
+
+/* The algorithm an allreduce of n elements of type t per rank over nranks
+ * ranks uses: LPC_ALGO_DDA_FLAT for bf16 up to LPC_DDA_FLAT_MAX_BYTES;
+ * LPC_ALGO_LOW_PRECISION from LPC_LOW_PRECISION_MIN_BYTES when
+ * low_precision_enabled != 0 and n is a multiple of 128*nranks;
+ * LPC_ALGO_DDA_TREE otherwise when n is a multiple of 8*nranks; else
+ * LPC_ALGO_DDA_FLAT for bf16.  Returns LPC_ALGO_AUTO when no algorithm
+ * applies (bad arguments, or fp32 with n not a multiple of 8*nranks).
+ * Pure function of its arguments, no HIP call.                              */
+lpc_algo lpc_select_algo(int nranks, size_t n, lpc_dtype t, int low_precision_enabled);
+
+/* Device workspace lpc_allreduce_emulated needs for (algo, nranks, n, t):
+ *   DDA flat:       nranks outputs of n elements
+ *   DDA tree:       nranks reduced chunks of n/nranks elements
+ *   low precision:  nranks quantized buffers (n codes + n/128 scales) and
+ *                   nranks requantized chunks, each region 256-byte aligned
+ * Writes the byte count to *bytes.  Errors as for lpc_allreduce_emulated,
+ * checked without HIP calls; LPC_ALGO_AUTO is LPC_ERR_DTYPE here.          */
+lpc_status lpc_allreduce_workspace_bytes(lpc_algo algo, int nranks, size_t n, lpc_dtype t, size_t *bytes);
+
+/* In-place allreduce (SUM) over nranks emulated ranks on one GPU: every
+ * bufs[r] ends with the elementwise sum over ranks, as the pages' Torchcomms
+ * allreduce(t, SUM) leaves it on every rank.  Each rank's share runs as that
+ * rank would run it, with the other ranks' buffers as its peers:
+ *   DDA flat:      every rank's dda_flat_reduce into its workspace output,
+ *                  then each output is copied into that rank's buffer;
+ *   DDA tree:      every rank's dda_tree_reduce_scatter into the workspace,
+ *                  then every rank's dda_tree_allgather into its buffer;
+ *   low precision: every rank's lpc_quantize_fp8, every rank's
+ *                  lpc_reduce_scatter_chunk, then every rank's
+ *                  lpc_allgather_dequant into its buffer (two quantizations).
+ * Results are those of the per-rank entry points, bit for bit.
+ *   bufs[r]    [n] of type t, device; distinct, non-overlapping
+ *   algo       not LPC_ALGO_AUTO (LPC_ERR_DTYPE); LPC_ALGO_DDA_FLAT needs
+ *              bf16 (LPC_ERR_DTYPE); shapes as the entry points it calls
+ *   workspace  device, 16-byte aligned, at least the bytes
+ *              lpc_allreduce_workspace_bytes gives (else LPC_ERR_SHAPE)
+ * The work is enqueued on `stream`; nothing is enqueued on error.          */
+lpc_status lpc_allreduce_emulated(void *const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Codec and library info                                                   */
 /* ---------------------------------------------------------------------- */
 

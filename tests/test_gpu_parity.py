@@ -532,3 +532,81 @@ def test_a2av_cfg5_full_sampled(dev, orc):
         assert_same(to_host(codes[k]), c, "cfg5 packed row %d codes" % k)
         assert_same(to_host(scales[k]), s, "cfg5 packed row %d scales" % k)
         assert_same(to_host(back[k]), orc.dequantize(c, s, bf16=True), "cfg5 dequant row %d" % k)
+
+
+# -- emulated allreduce (size-based dispatch, torchcomms-shaped wrapper) ------------------------------
+
+def _oracle_allreduce(orc, xs, algo, bf16):
+    N = len(xs)
+    if algo == lpc.ALGO_DDA_FLAT:
+        return orc.dda_flat(xs)
+    if algo == lpc.ALGO_DDA_TREE:
+        return np.concatenate([orc.dda_tree_rs(xs, r, bf16) for r in range(N)])
+    return orc.lp_allreduce(xs, bf16=bf16)["out"]
+
+
+@pytest.mark.parametrize("algo", [lpc.ALGO_DDA_FLAT, lpc.ALGO_DDA_TREE, lpc.ALGO_LOW_PRECISION],
+                         ids=["dda_flat", "dda_tree", "low_precision"])
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N", [2, 5, 8])
+def test_allreduce_emulated(dev, orc, algo, bf16, N):
+    """Every rank's buffer after lpc_allreduce_emulated equals the oracle's result of
+    the same algorithm (DDA flat is bf16 only)."""
+    if algo == lpc.ALGO_DDA_FLAT and not bf16:
+        pytest.skip("DDA flat reduces bf16 only")
+    n = BLOCK * N * 23
+    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    if bf16:
+        xs = [inputs.truncate_to_bf16(x) for x in xs]
+    say("allreduce emulated algo=%s N=%d n=%d bf16=%s" % (lpc.ALGO_NAMES[algo], N, n, bf16))
+    bufs = [to_dev(x, dev) for x in xs]
+    dt = bufs[0].dtype
+    ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, n, dt), dtype=torch.uint8, device=dev)
+    lpc.lpc_allreduce_emulated(bufs, algo, ws)
+    torch.cuda.synchronize()
+    ref = _oracle_allreduce(orc, xs, algo, bf16)
+    for r in range(N):
+        assert_same(to_host(bufs[r]), ref, "allreduce %s rank %d" % (lpc.ALGO_NAMES[algo], r))
+
+
+def test_allreduce_emulated_full_size_lp(dev, orc):
+    """Workload 3 at full size through the emulated allreduce (low precision): every
+    rank's buffer equals the oracle's allreduce output."""
+    N = 8
+    xs = [inputs.rank_buffer(3, r) for r in range(N)]
+    say("allreduce emulated low precision, N=8 x 16 MiB")
+    bufs = [to_dev(x, dev) for x in xs]
+    algo = lpc.lpc_select_algo(N, xs[0].size, torch.float32, True)
+    assert algo == lpc.ALGO_LOW_PRECISION
+    ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, xs[0].size, torch.float32), dtype=torch.uint8,
+                     device=dev)
+    lpc.lpc_allreduce_emulated(bufs, algo, ws)
+    torch.cuda.synchronize()
+    ref = orc.lp_allreduce(xs)["out"]
+    for r in range(N):
+        assert_same(to_host(bufs[r]), ref, "16 MiB LP allreduce rank %d" % r)
+
+
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_comm_pages_quickstart(dev, N):
+    """The pages' quick-start through the torchcomms-shaped wrapper: every rank fills a
+    10x20 tensor with its rank and calls allreduce(SUM) in place; every element of every
+    rank must be N(N-1)/2, whichever algorithm runs (forced ones pad to their unit)."""
+    import json
+    import os
+    from fp8_precision_allreduce_amd import comm
+
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "torchcomms_quickstart_allreduce.json")))
+    expect = [c["expected_every_element"] for c in gold["cases"] if c["nranks"] == N][0]
+    c = comm.new_comm("lpc", dev, "main_comm", nranks=N, low_precision=True)
+    runs = [(torch.float32, None), (torch.float32, lpc.ALGO_DDA_TREE), (torch.float32, lpc.ALGO_LOW_PRECISION),
+            (torch.bfloat16, None), (torch.bfloat16, lpc.ALGO_DDA_FLAT), (torch.bfloat16, lpc.ALGO_LOW_PRECISION)]
+    for dt, algo in runs:
+        say("pages quick-start via comm N=%d dtype=%s algo=%s" % (N, dt, algo))
+        ts = [torch.full((10, 20), float(r), dtype=dt, device=dev) for r in range(c.get_size())]
+        used = c.allreduce(ts, comm.ReduceOp.SUM, async_op=False, algo=algo)
+        if algo is not None:
+            assert used == algo
+        for t in ts:
+            assert t.shape == (10, 20)
+            assert torch.all(t.float() == expect), (dt, algo, t.float().unique())
