@@ -4,11 +4,13 @@
 //   * granule (quantize): one lane owns 16 contiguous elements, so the 8
 //     adjacent lanes of a wavefront-aligned group own one 128-element scale
 //     block; the block absmax is reduced across those 8 lanes with DPP.
-//   * quad (reduce-scatter, all-gather, dequantize): one lane owns 4
-//     contiguous elements, so a wavefront's loads and stores are single
-//     contiguous runs (256 codes, 1 KiB of fp32) and 32 lanes own a block;
-//     the absmax is reduced with DPP inside each 16-lane row and one
-//     ds_swizzle between the two rows of the half-wavefront.
+//   * lane vector of W elements (reduce-scatter, all-gather, dequantize, fused):
+//     one lane owns W contiguous elements, chosen so that a lane writes 16
+//     bytes of output (W = 4 for fp32, 8 for bf16; 4 where the output is
+//     codes), and a wavefront's loads and stores are single contiguous runs.
+//     128/W lanes own a block (32 or 16); the absmax is reduced with DPP
+//     inside each 16-lane row and, for W = 4, one ds_swizzle between the two
+//     rows of the half-wavefront.
 // No kernel allocates LDS for these reductions.
 //
 // FP8 is OCP E4M3FN (the gfx950 native FP8 format): the conversions below use
@@ -32,10 +34,15 @@ namespace lpc {
 constexpr int kBlock = 128;        // elements per scale
 constexpr int kGranule = 16;       // elements per lane (granule layout)
 constexpr int kLanesPerBlock = kBlock / kGranule;  // 8
-constexpr int kQuad = 4;           // elements per lane (quad layout)
+constexpr int kQuad = 4;           // elements per lane (lane vector of 4)
 constexpr int kLanesPerBlockQ = kBlock / kQuad;    // 32
 constexpr float kFp8Max = 448.0f;
 constexpr int kMaxRanks = 8;
+
+// clang vector types: the forms the non-temporal load/store builtins accept
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct RankCodes {
     const uint8_t* codes[kMaxRanks];
@@ -62,15 +69,21 @@ __device__ __forceinline__ float group8_max(float v) {
     return v;
 }
 
-// Max over the 32-lane half-wavefront of a block in the quad layout:
+// Max over a 16-lane row (a block in the 8-wide lane layout): group8_max,
+// then row_mirror (lane i <-> 15-i joins the two 8-lane halves of the row).
+__device__ __forceinline__ float group16_max(float v) {
+    v = group8_max(v);
+    const int x = __float_as_int(v);
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false)));
+}
+
+// Max over the 32-lane half-wavefront of a block in the 4-wide lane layout:
 // group8_max, then row_mirror (lane i <-> 15-i: joins the two 8-lane halves
 // of a row), then ds_swizzle in bit mode with xor mask 16 (swaps the two
 // 16-lane rows of each 32-lane group).
 __device__ __forceinline__ float group32_max(float v) {
-    v = group8_max(v);
-    int x = __float_as_int(v);
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false)));
-    x = __float_as_int(v);
+    v = group16_max(v);
+    const int x = __float_as_int(v);
     constexpr int kSwapRows = 0x1F | (0x10 << 10);  // and_mask 0x1F, or_mask 0, xor_mask 0x10
     return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(x, kSwapRows)));
 }
@@ -155,6 +168,61 @@ __device__ __forceinline__ uint32_t quantize_quad(const float (&v)[kQuad], float
     return encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
 }
 
+// ---------------------------------------------------------------------------
+// lane vectors of W = 4 or 8 elements
+// ---------------------------------------------------------------------------
+
+template <int W> struct LaneCodes;
+template <> struct LaneCodes<4> { using T = uint32_t; };
+template <> struct LaneCodes<8> { using T = uint2; };
+
+// Elements per lane that make one lane's output 16 bytes.
+template <typename Out> constexpr int lane_width() { return 16 / (int)sizeof(Out); }
+
+// W codes; NT = non-temporal (streaming) load
+template <int W, bool NT>
+__device__ __forceinline__ typename LaneCodes<W>::T load_codes(const uint8_t* __restrict__ p) {
+    if constexpr (W == 4) {
+        if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        else return *reinterpret_cast<const uint32_t*>(p);
+    } else {
+        if constexpr (NT) {
+            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+            return make_uint2(v.x, v.y);
+        } else {
+            return *reinterpret_cast<const uint2*>(p);
+        }
+    }
+}
+
+template <int W>
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ p, typename LaneCodes<W>::T c) {
+    *reinterpret_cast<typename LaneCodes<W>::T*>(p) = c;
+}
+
+// d[j] = fl32(E4M3(code j) * s)
+__device__ __forceinline__ void dequant_lane(uint32_t c, float s, float (&d)[4]) { dequant4(c, s, d); }
+__device__ __forceinline__ void dequant_lane(uint2 c, float s, float (&d)[8]) {
+    decode4(c.x, d);
+    decode4(c.y, d + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = d[j] * s;
+}
+
+// Blockwise quantization of a lane vector whose 128/W-lane group forms one
+// block: returns the codes and sets *scale (identical across the group).
+__device__ __forceinline__ uint32_t quantize_lane(const float (&v)[4], float* scale) { return quantize_quad(v, scale); }
+__device__ __forceinline__ uint2 quantize_lane(const float (&v)[8], float* scale) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group16_max(amax);
+    const float s = amax / kFp8Max;
+    *scale = s;
+    if (s == 0.0f) return make_uint2(0u, 0u);
+    return make_uint2(encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s), encode4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
+}
+
 // Blockwise quantization of a granule whose 8-lane group forms one block:
 // returns the codes and sets *scale (identical in all 8 lanes).
 __device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], float* scale) {
@@ -217,9 +285,6 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&v
 // quad stores (non-temporal)
 // ---------------------------------------------------------------------------
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void store_quad_nt(float* __restrict__ p, const float (&d)[kQuad]) {
     const f32x4_t v = {d[0], d[1], d[2], d[3]};
@@ -230,6 +295,15 @@ __device__ __forceinline__ void store_quad_nt(uint16_t* __restrict__ p, const fl
     const u32x2_t v = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
+
+// 16-byte non-temporal stores of a lane's output (W = 4 fp32, W = 8 bf16)
+__device__ __forceinline__ void store_lane_nt(float* __restrict__ p, const float (&d)[4]) { store_quad_nt(p, d); }
+__device__ __forceinline__ void store_lane_nt(uint16_t* __restrict__ p, const float (&d)[8]) {
+    const u32x4_t v = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]),
+                       pack_bf16x2(d[6], d[7])};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_lane_nt(uint16_t* __restrict__ p, const float (&d)[4]) { store_quad_nt(p, d); }
 
 __device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[kGranule]) {
     float4* q = reinterpret_cast<float4*>(p);

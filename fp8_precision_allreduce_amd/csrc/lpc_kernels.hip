@@ -4,8 +4,8 @@
 //
 // The quantizers use one 16-element granule per lane (a wavefront covers 8
 // scale blocks); the reduce-scatter, all-gather, fused and dequantize kernels
-// use one 4-element quad per lane (a wavefront covers 2 blocks), see
-// lpc_device.hpp.  Streaming kernels use 256-lane workgroups.  Rank loops are
+// give each lane a vector of 4 or 8 elements, so that every lane writes 16
+// bytes (see lpc_device.hpp).  Streaming kernels use 256-lane workgroups.  Rank loops are
 // unrolled by template parameter so that all N loads of a lane are in flight
 // before the first add.
 #include "lpc_device.hpp"
@@ -62,77 +62,85 @@ hipError_t launch_quantize(const void* x, int in_bf16, size_t n, uint8_t* codes,
 }
 
 // ---------------------------------------------------------------------------
-// Quad-layout kernels: one lane owns 4 contiguous elements of a chunk, 32
-// lanes a scale block; tiles are taken in XCD-aware order.
+// Lane-vector kernels: one lane owns W contiguous elements of a chunk (W = 4
+// when the lane writes fp32 or codes, 8 when it writes bf16, so that every
+// lane stores 16 bytes), 128/W lanes a scale block; tiles are taken in
+// XCD-aware order.
 // ---------------------------------------------------------------------------
 
-static inline dim3 quad_grid(size_t elems, unsigned y = 1) {
-    const size_t lanes = elems / kQuad;
+template <int W>
+static inline dim3 lane_grid(size_t elems, unsigned y = 1) {
+    const size_t lanes = elems / W;
     return dim3((unsigned)((lanes + kThreads - 1) / kThreads), y, 1);
 }
 
-__device__ __forceinline__ size_t quad_elem() {
-    return (xcd_tile() * kThreads + threadIdx.x) * kQuad;
+template <int W>
+__device__ __forceinline__ size_t lane_elem() {
+    return (xcd_tile() * kThreads + threadIdx.x) * W;
 }
 
-// Rank-order FP32 sum of the quad at rank-buffer offset e over N ranks: all
-// N code and scale loads are issued before the first add.
-template <int N>
-__device__ __forceinline__ void rank_sum4(const RankCodes& in, size_t e, float (&acc)[kQuad]) {
-    uint32_t c[N];
+// Rank-order FP32 sum of the W elements at rank-buffer offset e over N ranks:
+// all N code and scale loads are issued before the first add.
+template <int N, int W>
+__device__ __forceinline__ void rank_sum(const RankCodes& in, size_t e, float (&acc)[W]) {
+    typename LaneCodes<W>::T c[N];
     float s[N];
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-        c[p] = *reinterpret_cast<const uint32_t*>(in.codes[p] + e);
+        c[p] = load_codes<W, false>(in.codes[p] + e);
         s[p] = in.scales[p][e / kBlock];
     }
-    dequant4(c[0], s[0], acc);
+    dequant_lane(c[0], s[0], acc);
 #pragma unroll
     for (int p = 1; p < N; ++p) {
-        float d[kQuad];
-        dequant4(c[p], s[p], d);
+        float d[W];
+        dequant_lane(c[p], s[p], d);
 #pragma unroll
-        for (int j = 0; j < kQuad; ++j) acc[j] = acc[j] + d[j];
+        for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
     }
 }
 
 // ---------------------------------------------------------------------------
 // (2) reduce-scatter step: N-way dequant + rank-order FP32 sum of one chunk,
-// requantized (kRequant) or written out as the sum (kSumF32 / kSumBF16).
+// requantized (kRequant, W = 4) or written out as the sum (kSumF32, W = 4;
+// kSumBF16, W = 8).
 // ---------------------------------------------------------------------------
 
 enum RsOut { kRequant = 0, kSumF32 = 1, kSumBF16 = 2 };
+
+template <int Mode> constexpr int rs_width() { return Mode == kSumBF16 ? 8 : 4; }
 
 template <int N, int Mode>
 __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RankCodes in, size_t chunk_off, size_t C,
                                                                   uint8_t* __restrict__ cc,
                                                                   float* __restrict__ cs,
                                                                   void* __restrict__ out) {
-    const size_t i = quad_elem();
-    if (i >= C) return;  // whole 32-lane blocks drop out together (C % 128 == 0)
-    float acc[kQuad];
-    rank_sum4<N>(in, chunk_off + i, acc);
-    if (Mode == kRequant) {
+    constexpr int W = rs_width<Mode>();
+    const size_t i = lane_elem<W>();
+    if (i >= C) return;  // whole blocks of 128/W lanes drop out together (C % 128 == 0)
+    float acc[W];
+    rank_sum<N, W>(in, chunk_off + i, acc);
+    if constexpr (Mode == kRequant) {
         float s;
-        const uint32_t c = quantize_quad(acc, &s);
-        *reinterpret_cast<uint32_t*>(cc + i) = c;
-        if ((threadIdx.x & (kLanesPerBlockQ - 1)) == 0) cs[i / kBlock] = s;
-    } else if (Mode == kSumF32) {
-        store_quad_nt(static_cast<float*>(out) + i, acc);
+        const auto c = quantize_lane(acc, &s);
+        store_codes<W>(cc + i, c);
+        if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = s;
+    } else if constexpr (Mode == kSumF32) {
+        store_lane_nt(static_cast<float*>(out) + i, acc);
     } else {
-        store_quad_nt(static_cast<uint16_t*>(out) + i, acc);
+        store_lane_nt(static_cast<uint16_t*>(out) + i, acc);
     }
 }
 
 template <int Mode>
 static void launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_t C, uint8_t* cc, float* cs,
                         void* out, hipStream_t stream) {
-    const dim3 grid = quad_grid(C), block(kThreads);
+    const dim3 grid = lane_grid<rs_width<Mode>()>(C), block(kThreads);
     switch (nranks) {
 #define LPC_RS_CASE(NR)                                                                              \
     case NR:                                                                                         \
-        launch((reduce_scatter_kernel<NR, Mode>), grid, block, 0, stream, in, chunk_off, \
-                           C, cc, cs, out);                                                          \
+        launch((reduce_scatter_kernel<NR, Mode>), grid, block, 0, stream, in, chunk_off, C, cc, cs,  \
+               out);                                                                                 \
         break;
         LPC_RS_CASE(1) LPC_RS_CASE(2) LPC_RS_CASE(3) LPC_RS_CASE(4)
         LPC_RS_CASE(5) LPC_RS_CASE(6) LPC_RS_CASE(7) LPC_RS_CASE(8)
@@ -164,24 +172,24 @@ hipError_t launch_reduce_scatter_out(const RankCodes& in, int nranks, int rank, 
 template <typename Out>
 __global__ __launch_bounds__(kThreads) void allgather_kernel(RankCodes chunks, size_t C,
                                                              Out* __restrict__ out) {
-    const size_t i = quad_elem();
+    constexpr int W = lane_width<Out>();
+    const size_t i = lane_elem<W>();
     if (i >= C) return;
     const int p = blockIdx.y;
-    const uint32_t c = *reinterpret_cast<const uint32_t*>(chunks.codes[p] + i);
-    float d[kQuad];
-    dequant4(c, chunks.scales[p][i / kBlock], d);
-    store_quad_nt(out + (size_t)p * C + i, d);
+    float d[W];
+    dequant_lane(load_codes<W, false>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
+    store_lane_nt(out + (size_t)p * C + i, d);
 }
 
 hipError_t launch_allgather(const RankCodes& chunks, int nranks, size_t n, void* out, int out_bf16,
                             hipStream_t stream) {
     const size_t C = n / nranks;
     if (out_bf16)
-        launch(allgather_kernel<uint16_t>, quad_grid(C, nranks), dim3(kThreads), 0, stream,
-                           chunks, C, static_cast<uint16_t*>(out));
+        launch(allgather_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(C, nranks), dim3(kThreads), 0,
+               stream, chunks, C, static_cast<uint16_t*>(out));
     else
-        launch(allgather_kernel<float>, quad_grid(C, nranks), dim3(kThreads), 0, stream,
-                           chunks, C, static_cast<float*>(out));
+        launch(allgather_kernel<float>, lane_grid<lane_width<float>()>(C, nranks), dim3(kThreads), 0, stream,
+               chunks, C, static_cast<float*>(out));
     return hipGetLastError();
 }
 
@@ -189,31 +197,34 @@ template <typename Out>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales, size_t n,
                                                            Out* __restrict__ out) {
-    const size_t i = quad_elem();
+    constexpr int W = lane_width<Out>();
+    const size_t i = lane_elem<W>();
     if (i >= n) return;
-    float d[kQuad];
-    dequant4(*reinterpret_cast<const uint32_t*>(codes + i), scales[i / kBlock], d);
-    store_quad_nt(out + i, d);
+    float d[W];
+    dequant_lane(load_codes<W, false>(codes + i), scales[i / kBlock], d);
+    store_lane_nt(out + i, d);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, void* out, int out_bf16,
                           hipStream_t stream) {
     if (out_bf16)
-        launch(dequant_kernel<uint16_t>, quad_grid(n), dim3(kThreads), 0, stream, codes, scales,
-                           n, static_cast<uint16_t*>(out));
+        launch(dequant_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(n), dim3(kThreads), 0, stream, codes,
+               scales, n, static_cast<uint16_t*>(out));
     else
-        launch(dequant_kernel<float>, quad_grid(n), dim3(kThreads), 0, stream, codes, scales,
-                           n, static_cast<float*>(out));
+        launch(dequant_kernel<float>, lane_grid<lane_width<float>()>(n), dim3(kThreads), 0, stream, codes,
+               scales, n, static_cast<float*>(out));
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// (2)+(3) fused.  Every lane owns the same quad position i of every chunk.
-// The peers' chunks are split into slices of two (peer q = rank + 1 ..
-// rank + N - 1, mod N): grid.y == 0 reduces and requantizes the own chunk at
-// i, writes its dequantization from registers, and dequantizes peers q = 1, 2
-// at i; grid.y == y > 0 dequantizes peers q = 2y + 1, 2y + 2.  Each lane issues
-// all of its loads before its first conversion.
+// (2)+(3) fused.  Every lane owns the same position i of every chunk.  The
+// peers' chunks are split into slices of two (peer q = rank + 1 .. rank + N - 1,
+// mod N): grid.y == 0 reduces and requantizes the own chunk at i, writes its
+// dequantization from registers, and dequantizes peers q = 1, 2 at i;
+// grid.y == y > 0 dequantizes peers q = 2y + 1, 2y + 2.  Each lane issues all
+// of its loads before its first conversion.  With bf16 output (W = 8) the
+// code loads are non-temporal: 15 streams are read once each, and keeping
+// them out of the caches measured faster at large sizes.
 // ---------------------------------------------------------------------------
 
 constexpr int kPeersPerSlice = 2;
@@ -227,11 +238,14 @@ __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, Ran
                                                                size_t C, uint8_t* __restrict__ cc,
                                                                float* __restrict__ cs,
                                                                Out* __restrict__ out) {
-    const size_t i = quad_elem();
+    constexpr int W = lane_width<Out>();
+    constexpr bool kNtLoads = W == 8;
+    using Codes = typename LaneCodes<W>::T;
+    const size_t i = lane_elem<W>();
     if (i >= C) return;
     const int y = blockIdx.y;
     const int q_first = kPeersPerSlice * y + 1;
-    uint32_t pc[kPeersPerSlice];
+    Codes pc[kPeersPerSlice];
     float ps[kPeersPerSlice];
     int pp[kPeersPerSlice];
 #pragma unroll
@@ -240,42 +254,42 @@ __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, Ran
         if (p >= N) p -= N;
         pp[k] = p;
     }
-    float d[kQuad];
+    float d[W];
     if (y == 0) {
         const size_t own = (size_t)rank * C + i;
-        uint32_t c[N];
+        Codes c[N];
         float s[N];
 #pragma unroll
         for (int p = 0; p < N; ++p) {
-            c[p] = *reinterpret_cast<const uint32_t*>(in.codes[p] + own);
+            c[p] = load_codes<W, kNtLoads>(in.codes[p] + own);
             s[p] = in.scales[p][own / kBlock];
         }
 #pragma unroll
         for (int k = 0; k < kPeersPerSlice; ++k) {
             if (q_first + k < N) {
-                pc[k] = *reinterpret_cast<const uint32_t*>(peers.codes[pp[k]] + i);
+                pc[k] = load_codes<W, kNtLoads>(peers.codes[pp[k]] + i);
                 ps[k] = peers.scales[pp[k]][i / kBlock];
             }
         }
-        float acc[kQuad];
-        dequant4(c[0], s[0], acc);
+        float acc[W];
+        dequant_lane(c[0], s[0], acc);
 #pragma unroll
         for (int p = 1; p < N; ++p) {
-            dequant4(c[p], s[p], d);
+            dequant_lane(c[p], s[p], d);
 #pragma unroll
-            for (int j = 0; j < kQuad; ++j) acc[j] = acc[j] + d[j];
+            for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
         }
         float sc;
-        const uint32_t code = quantize_quad(acc, &sc);
-        *reinterpret_cast<uint32_t*>(cc + i) = code;
-        if ((threadIdx.x & (kLanesPerBlockQ - 1)) == 0) cs[i / kBlock] = sc;
-        dequant4(code, sc, d);  // own chunk straight from registers
-        store_quad_nt(out + own, d);
+        const Codes code = quantize_lane(acc, &sc);
+        store_codes<W>(cc + i, code);
+        if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = sc;
+        dequant_lane(code, sc, d);  // own chunk straight from registers
+        store_lane_nt(out + own, d);
     } else {
 #pragma unroll
         for (int k = 0; k < kPeersPerSlice; ++k) {
             if (q_first + k < N) {
-                pc[k] = *reinterpret_cast<const uint32_t*>(peers.codes[pp[k]] + i);
+                pc[k] = load_codes<W, kNtLoads>(peers.codes[pp[k]] + i);
                 ps[k] = peers.scales[pp[k]][i / kBlock];
             }
         }
@@ -283,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, Ran
 #pragma unroll
     for (int k = 0; k < kPeersPerSlice; ++k) {
         if (q_first + k < N) {
-            dequant4(pc[k], ps[k], d);
-            store_quad_nt(out + (size_t)pp[k] * C + i, d);
+            dequant_lane(pc[k], ps[k], d);
+            store_lane_nt(out + (size_t)pp[k] * C + i, d);
         }
     }
 }
@@ -293,15 +307,17 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
                               uint8_t* cc, float* cs, void* out, int out_bf16, hipStream_t stream) {
     const size_t C = n / nranks;
     const dim3 block(kThreads);
+    const dim3 grid_f32 = lane_grid<lane_width<float>()>(C, fused_slices(nranks));
+    const dim3 grid_bf16 = lane_grid<lane_width<uint16_t>()>(C, fused_slices(nranks));
     switch (nranks) {
-#define LPC_FUSED_CASE(NR)                                                                               \
-    case NR:                                                                                             \
-        if (out_bf16)                                                                                    \
-            launch((rs_ag_fused_kernel<NR, uint16_t>), quad_grid(C, fused_slices(NR)), block, \
-                               0, stream, in, peers, rank, C, cc, cs, static_cast<uint16_t*>(out));      \
-        else                                                                                             \
-            launch((rs_ag_fused_kernel<NR, float>), quad_grid(C, fused_slices(NR)), block,   \
-                               0, stream, in, peers, rank, C, cc, cs, static_cast<float*>(out));         \
+#define LPC_FUSED_CASE(NR)                                                                           \
+    case NR:                                                                                         \
+        if (out_bf16)                                                                                \
+            launch((rs_ag_fused_kernel<NR, uint16_t>), grid_bf16, block, 0, stream, in, peers, rank, \
+                   C, cc, cs, static_cast<uint16_t*>(out));                                          \
+        else                                                                                         \
+            launch((rs_ag_fused_kernel<NR, float>), grid_f32, block, 0, stream, in, peers, rank, C,  \
+                   cc, cs, static_cast<float*>(out));                                                \
         break;
         LPC_FUSED_CASE(1) LPC_FUSED_CASE(2) LPC_FUSED_CASE(3) LPC_FUSED_CASE(4)
         LPC_FUSED_CASE(5) LPC_FUSED_CASE(6) LPC_FUSED_CASE(7) LPC_FUSED_CASE(8)
@@ -455,101 +471,137 @@ hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size
 }
 
 // ---------------------------------------------------------------------------
-// all-to-all-v routing: one workgroup of 1024 lanes.  Lane t owns rows
-// [t*R, (t+1)*R).  Per-lane destination counts go to LDS, one wavefront per
-// destination turns them into exclusive prefixes, and each lane then places
-// its rows in order: a stable destination-major permutation.
+// all-to-all-v routing: one workgroup of 1024 lanes (16 wavefronts).  Rows are
+// taken in super-tiles of 16 x 1024: lane t holds rows st + b*1024 + t,
+// b = 0..15, in registers (one batch of loads, then no global reads), so a
+// super-tile costs one load latency.
+//   pass 1: per-destination counts, from wavefront ballots; counts, and
+//           offsets as their exclusive prefix.
+//   pass 2: for each super-tile, the ballots give every row its rank among
+//           the earlier lanes of its wavefront with the same destination, and
+//           every (b, wavefront) its count per destination; an exclusive
+//           prefix over (b, wavefront) in row order, started at the
+//           destination's running base, places each row: a stable,
+//           destination-major permutation.
 // ---------------------------------------------------------------------------
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteBatch = 16;
+constexpr size_t kRouteSuperTile = (size_t)kRouteBatch * kRouteThreads;
+
+// number of lanes below this one whose bit is set in mask
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ void load_route_batch(const int32_t* __restrict__ dest, size_t rows, size_t st,
+                                                 int nranks, int32_t (&d)[kRouteBatch]) {
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+        const size_t k = st + (size_t)b * kRouteThreads + threadIdx.x;
+        const int32_t v = k < rows ? dest[k] : -1;
+        d[b] = (v >= 0 && v < nranks) ? v : -1;  // out-of-range destinations are dropped
+    }
+}
 
 __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t* __restrict__ dest,
                                                                    size_t rows, int nranks,
                                                                    int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ perm) {
-    __shared__ int32_t pre[kMaxRanks][kRouteThreads];
-    __shared__ int32_t total[kMaxRanks];
+    __shared__ int32_t wave_cnt[kRouteBatch][kRouteWaves][kMaxRanks];  // then the in-batch prefix
+    __shared__ int32_t batch_base[kRouteBatch][kMaxRanks];
     __shared__ int32_t base[kMaxRanks];
-    const int t = threadIdx.x;
-    const size_t R = (rows + kRouteThreads - 1) / kRouteThreads;
-    const size_t k0 = (size_t)t * R;
-    const size_t k1 = k0 + R < rows ? k0 + R : rows;
+    __shared__ int32_t placed;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int32_t d[kRouteBatch];
 
+    // pass 1: counts
     int32_t cnt[kMaxRanks];
 #pragma unroll
-    for (int d = 0; d < kMaxRanks; ++d) cnt[d] = 0;
-    for (size_t k = k0; k < k1; ++k) {
-        const int32_t d = dest[k];
+    for (int j = 0; j < kMaxRanks; ++j) cnt[j] = 0;
+    for (size_t st = 0; st < rows; st += kRouteSuperTile) {
+        load_route_batch(dest, rows, st, nranks, d);
 #pragma unroll
-        for (int j = 0; j < kMaxRanks; ++j) cnt[j] += (d == j && j < nranks) ? 1 : 0;
+        for (int b = 0; b < kRouteBatch; ++b)
+#pragma unroll
+            for (int j = 0; j < kMaxRanks; ++j) cnt[j] += __popcll(__ballot(d[b] == j));
     }
+    if (lane == 0) {
 #pragma unroll
-    for (int d = 0; d < kMaxRanks; ++d) pre[d][t] = cnt[d];
-    __syncthreads();
-
-    // wavefront w < 8 scans destination w: lane l owns entries [16l, 16l+16)
-    const int w = t / 64, lane = t % 64;
-    if (w < kMaxRanks) {
-        int32_t* row = pre[w];
-        int32_t local[16];
-        int32_t sum = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            local[i] = row[lane * 16 + i];
-            sum += local[i];
-        }
-        // inclusive scan of per-lane sums across the wavefront
-        int32_t inc = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += y;
-        }
-        int32_t run = inc - sum;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            row[lane * 16 + i] = run;
-            run += local[i];
-        }
-        if (lane == 63) total[w] = inc;
+        for (int j = 0; j < kMaxRanks; ++j) wave_cnt[0][w][j] = cnt[j];
     }
     __syncthreads();
     if (t == 0) {
         int32_t acc = 0;
-        for (int d = 0; d < kMaxRanks; ++d) {
-            base[d] = acc;
-            if (d < nranks) {
-                counts[d] = total[d];
-                offsets[d] = acc;
-                acc += total[d];
+        for (int j = 0; j < kMaxRanks; ++j) {
+            int32_t c = 0;
+            for (int v = 0; v < kRouteWaves; ++v) c += wave_cnt[0][v][j];
+            base[j] = acc;
+            if (j < nranks) {
+                counts[j] = c;
+                offsets[j] = acc;
+                acc += c;
             }
         }
+        placed = acc;
     }
     __syncthreads();
-    int32_t pos[kMaxRanks];
+
+    // pass 2: stable scatter, one super-tile at a time
+    for (size_t st = 0; st < rows; st += kRouteSuperTile) {
+        load_route_batch(dest, rows, st, nranks, d);
+        int32_t rank_in_wave[kRouteBatch];
 #pragma unroll
-    for (int d = 0; d < kMaxRanks; ++d) pos[d] = base[d] + pre[d][t];
-    for (size_t k = k0; k < k1; ++k) {
-        const int32_t d = dest[k];
+        for (int b = 0; b < kRouteBatch; ++b) {
+            rank_in_wave[b] = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxRanks; ++j) {
-            if (d == j && j < nranks) {
-                perm[pos[j]] = (int32_t)k;
-                pos[j] += 1;
+            for (int j = 0; j < kMaxRanks; ++j) {
+                const uint64_t m = __ballot(d[b] == j);
+                if (d[b] == j) rank_in_wave[b] = lanes_below(m);
+                if (lane == 0) wave_cnt[b][w][j] = __popcll(m);
             }
         }
+        __syncthreads();
+        if (t < kRouteBatch * kMaxRanks) {  // (b, j): exclusive prefix over the wavefronts of batch b
+            const int b = t / kMaxRanks, j = t % kMaxRanks;
+            int32_t run = 0;
+            for (int v = 0; v < kRouteWaves; ++v) {
+                const int32_t c = wave_cnt[b][v][j];
+                wave_cnt[b][v][j] = run;
+                run += c;
+            }
+            batch_base[b][j] = run;
+        }
+        __syncthreads();
+        if (t < kMaxRanks) {  // j: exclusive prefix over the batches, from the running base
+            int32_t run = base[t];
+            for (int b = 0; b < kRouteBatch; ++b) {
+                const int32_t c = batch_base[b][t];
+                batch_base[b][t] = run;
+                run += c;
+            }
+            base[t] = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < kRouteBatch; ++b) {
+            if (d[b] >= 0) {
+                const size_t k = st + (size_t)b * kRouteThreads + t;
+                perm[batch_base[b][d[b]] + wave_cnt[b][w][d[b]] + rank_in_wave[b]] = (int32_t)k;
+            }
+        }
+        __syncthreads();  // the next super-tile rewrites wave_cnt and batch_base
     }
     // rows with an out-of-range destination were dropped: mark perm's tail
-    int32_t placed = 0;
-    for (int d = 0; d < nranks; ++d) placed += total[d];
     for (size_t k = (size_t)placed + t; k < rows; k += kRouteThreads) perm[k] = -1;
 }
 
 hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32_t* counts, int32_t* offsets,
                              int32_t* perm, hipStream_t stream) {
     launch(a2av_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, dest, rows, nranks, counts,
-                       offsets, perm);
+           offsets, perm);
     return hipGetLastError();
 }
 

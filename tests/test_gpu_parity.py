@@ -248,17 +248,20 @@ def test_lp_allreduce_rank_counts(dev, orc, N, bf16, fused):
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "N=%d" % N)
 
 
-@pytest.mark.parametrize("chunk_blocks", [1, 2, 7, 8, 9, 63, 64, 65, 8 * 64 + 3])
-def test_fused_chunk_sizes(dev, orc, chunk_blocks):
-    """Chunk sizes around the wavefront (2 blocks), workgroup (8 blocks) and XCD
-    (8 workgroups) granularities: every tile of the XCD-aware order is visited
-    exactly once."""
+@pytest.mark.parametrize("chunk_blocks", [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 63, 64, 65, 8 * 64 + 3])
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
+    """Chunk sizes around the wavefront (2 blocks of 4-wide lanes, 4 of 8-wide),
+    workgroup (8 or 16 blocks) and XCD (8 workgroups) granularities: every tile of
+    the XCD-aware order is visited exactly once, for both lane widths."""
     N = 8
     n = BLOCK * N * chunk_blocks
     xs = [inputs.rank_buffer(1, r, n) for r in range(N)]
-    say("fused chunk of %d blocks, N=8" % chunk_blocks)
-    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, True)
-    compare_allreduce(res, orc.lp_allreduce(xs), "chunk_blocks=%d" % chunk_blocks)
+    if bf16:
+        xs = [inputs.truncate_to_bf16(x) for x in xs]
+    say("fused chunk of %d blocks, N=8, bf16=%s" % (chunk_blocks, bf16))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.bfloat16 if bf16 else torch.float32, True)
+    compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "chunk_blocks=%d" % chunk_blocks)
 
 
 def test_graph_replays_match_eager(dev):
@@ -610,3 +613,24 @@ def test_comm_pages_quickstart(dev, N):
         for t in ts:
             assert t.shape == (10, 20)
             assert torch.all(t.float() == expect), (dt, algo, t.float().unique())
+
+
+def test_a2av_quantize_rows_more_than_grid_y(dev, orc):
+    """70,000 short rows: more rows than one launch's grid.y (65,535), so workgroups loop
+    over rows; perm from the router, checked in full against the oracle."""
+    rows, row_len = 70_000, 128
+    x = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(5, 2), rows * row_len, 1.0)).reshape(rows, row_len)
+    dest = inputs.zipf_destinations(rows=rows)
+    say("a2av quantize rows=%d row_len=%d" % (rows, row_len))
+    counts = torch.empty(8, dtype=torch.int32, device=dev)
+    offsets = torch.empty(8, dtype=torch.int32, device=dev)
+    perm = torch.empty(rows, dtype=torch.int32, device=dev)
+    lpc.lpc_a2av_route(to_dev(dest, dev), 8, counts, offsets, perm)
+    codes = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, 1), dtype=torch.float32, device=dev)
+    lpc.lpc_quantize_fp8_rows(to_dev(x, dev), perm, codes, scales)
+    _, _, rp = orc.a2av_route(dest, 8)
+    assert_same(to_host(perm), rp, "perm")
+    rc, rs = orc.quantize_rows(x, rp, bf16=True)
+    assert_same(to_host(codes), rc, "rows codes")
+    assert_same(to_host(scales), rs, "rows scales")
