@@ -142,10 +142,12 @@ def test_e4m3_encode_matches_oracle(dev, orc):
         assert_same(to_host(codes), orc.e4m3_encode(v[:n]), "encode n=%d" % n)
 
 
-@pytest.mark.parametrize("lo_exp,hi_exp", [(-12, -5), (7, 10)])
+@pytest.mark.parametrize("lo_exp,hi_exp", [(-12, -5), (-5, 1), (1, 7), (7, 10)])
 def test_e4m3_encode_every_float_in_binades(dev, orc, lo_exp, hi_exp):
-    """Every float32 pattern with exponent in [lo, hi): the E4M3 subnormal/tie region
-    and the top binade with saturation."""
+    """Every float32 pattern with exponent in [lo, hi), both signs: together the ranges
+    cover [2^-12, 2^10) in full -- everything below rounds to a signed zero, everything
+    above saturates -- so every E4M3 rounding decision of the conversion instruction,
+    subnormal, normal, tie and saturation, is compared with the oracle."""
     lo = np.uint32(f32bits(np.float32([2.0 ** lo_exp]))[0])
     hi = np.uint32(f32bits(np.float32([2.0 ** hi_exp]))[0])
     v = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
