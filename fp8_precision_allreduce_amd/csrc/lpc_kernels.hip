@@ -38,7 +38,7 @@ template <typename In>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict__ x, size_t ngran,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
-    const size_t g = granule_id();
+    const size_t g = xcd_tile() * kThreads + threadIdx.x;
     if (g >= ngran) return;  // whole 8-lane groups drop out together (n % 128 == 0)
     float v[kGranule];
     load16(x + g * kGranule, v);
@@ -606,54 +606,46 @@ hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32
 }
 
 // ---------------------------------------------------------------------------
-// gather + quantize rows: grid.y walks packed rows, grid.x the granules of a row
+// gather + quantize rows: flat granules over the packed (row, column) space,
+// in XCD-aware tile order.  A granule never straddles a row (row_len % 128 ==
+// 0); its source row is perm[packed row].  An invalid perm entry quantizes a
+// zero row: scale +0, codes 0x00.
 // ---------------------------------------------------------------------------
 
 template <typename In>
-__global__ __launch_bounds__(1024) void quantize_rows_kernel(const In* __restrict__ x, size_t rows,
-                                                             size_t row_len, const int32_t* __restrict__ perm,
-                                                             uint8_t* __restrict__ codes,
-                                                             float* __restrict__ scales) {
-    const size_t lpr = row_len / kGranule;
-    const size_t seg = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (seg >= lpr) return;
-    for (size_t k = blockIdx.y; k < rows; k += gridDim.y) {
-        const int32_t src = perm[k];
-        const size_t g = k * lpr + seg;  // packed granule index
-        if (src < 0 || (size_t)src >= rows) {
-            *reinterpret_cast<uint4*>(codes + g * kGranule) = make_uint4(0u, 0u, 0u, 0u);
-            if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = 0.0f;
-            continue;
-        }
-        float v[kGranule];
-        load16(x + (size_t)src * row_len + seg * kGranule, v);
-        float s;
-        const uint4 c = quantize_granule(v, &s);
-        *reinterpret_cast<uint4*>(codes + g * kGranule) = c;
-        if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const In* __restrict__ x, size_t rows,
+                                                                 size_t row_len, const int32_t* __restrict__ perm,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 float* __restrict__ scales) {
+    const size_t g = xcd_tile() * kThreads + threadIdx.x;  // packed granule index
+    const size_t e = g * kGranule;
+    if (e >= rows * row_len) return;  // whole 8-lane blocks drop out together
+    const size_t k = e / row_len;
+    const size_t col = e - k * row_len;
+    const int32_t src = perm[k];
+    float v[kGranule];
+    if (src < 0 || (size_t)src >= rows) {
+#pragma unroll
+        for (int j = 0; j < kGranule; ++j) v[j] = 0.0f;
+    } else {
+        load16(x + (size_t)src * row_len + col, v);
     }
+    float s;
+    const uint4 c = quantize_granule(v, &s);
+    const u32x4_t cv = {c.x, c.y, c.z, c.w};
+    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + e));
+    if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
 }
 
 hipError_t launch_quantize_rows(const void* x, int in_bf16, size_t rows, size_t row_len, const int32_t* perm,
                                 uint8_t* codes, float* scales, hipStream_t stream) {
-    const size_t lpr = row_len / kGranule;
-    // a row of up to 1024 granules is one workgroup (whole wavefronts); longer rows use 256-lane groups
-    unsigned threads, gx;
-    if (lpr <= 1024) {
-        threads = (unsigned)((lpr + 63) / 64 * 64);
-        gx = 1;
-    } else {
-        threads = kThreads;
-        gx = (unsigned)((lpr + kThreads - 1) / kThreads);
-    }
-    const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
-    const dim3 grid(gx, gy, 1), block(threads);
+    const dim3 grid = grid_for(rows * row_len / kGranule), block(kThreads);
     if (in_bf16)
-        launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x),
-                           rows, row_len, perm, codes, scales);
+        launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x), rows,
+               row_len, perm, codes, scales);
     else
-        launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows,
-                           row_len, perm, codes, scales);
+        launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows, row_len,
+               perm, codes, scales);
     return hipGetLastError();
 }
 

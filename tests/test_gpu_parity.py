@@ -636,3 +636,23 @@ def test_a2av_quantize_rows_more_than_grid_y(dev, orc):
     rc, rs = orc.quantize_rows(x, rp, bf16=True)
     assert_same(to_host(codes), rc, "rows codes")
     assert_same(to_host(scales), rs, "rows scales")
+
+
+def test_a2av_quantize_rows_f32(dev, orc):
+    """Row gather + quantize from fp32 rows (3 blocks per row), with invalid perm entries."""
+    rows, row_len = 257, 384
+    x = inputs.normal_f32(inputs.rng(5, 3), rows * row_len, 1.0).reshape(rows, row_len)
+    _, _, perm = orc.a2av_route(inputs.zipf_destinations(rows=rows), 8)
+    p = perm.copy()
+    p[3] = -7
+    p[200] = rows + 5
+    say("a2av quantize rows fp32 rows=%d row_len=%d" % (rows, row_len))
+    codes = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, row_len // BLOCK), dtype=torch.float32, device=dev)
+    lpc.lpc_quantize_fp8_rows(to_dev(x, dev), to_dev(p, dev), codes, scales)
+    rc, rs = orc.quantize_rows(x, perm, bf16=False)
+    for k in (3, 200):
+        rc[k] = 0
+        rs[k] = 0.0
+    assert_same(to_host(codes), rc, "fp32 rows codes")
+    assert_same(to_host(scales), rs, "fp32 rows scales")
