@@ -538,8 +538,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3/f32",
-        "data": "synthetic (seeded N(0,1) fp32 with 0.1% outliers x100; DDA: seeded N(0,0.5) bf16)",
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) fp32 with 0.1% outliers x100; DDA: seeded N(0,0.5) bf16); FP8 E4M3 storage, FP32 arithmetic",
         "config": {
             "workload": "lp_allreduce_n8_16MiB_f32 + dda_flat_n8_64KiB_bf16: rank 0's share of an N=8 FP8 "
                         "low-precision allreduce, 4,194,304 fp32 per rank, 128-element blocks, E4M3 + FP32 "
