@@ -34,8 +34,6 @@ namespace lpc {
 constexpr int kBlock = 128;        // elements per scale
 constexpr int kGranule = 16;       // elements per lane (granule layout)
 constexpr int kLanesPerBlock = kBlock / kGranule;  // 8
-constexpr int kQuad = 4;           // elements per lane (lane vector of 4)
-constexpr int kLanesPerBlockQ = kBlock / kQuad;    // 32
 constexpr float kFp8Max = 448.0f;
 constexpr int kMaxRanks = 8;
 
@@ -54,11 +52,12 @@ struct RankBufs {
 };
 
 // ---------------------------------------------------------------------------
-// cross-lane max over the 8-lane group of a 128-element block (DPP)
+// cross-lane block max (DPP inside 16-lane rows, ds_swizzle across rows)
 // ---------------------------------------------------------------------------
 
-// quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror
-// (lane i <-> 7-i inside each 8-lane half row: joins the two quads).
+// Max over each aligned group of 8 lanes: quad_perm [1,0,3,2] (xor 1),
+// quad_perm [2,3,0,1] (xor 2), row_half_mirror (lane i <-> 7-i inside each
+// 8-lane half row: joins the two quads).
 __device__ __forceinline__ float group8_max(float v) {
     int x = __float_as_int(v);
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)));
@@ -69,18 +68,16 @@ __device__ __forceinline__ float group8_max(float v) {
     return v;
 }
 
-// Max over a 16-lane row (a block in the 8-wide lane layout): group8_max,
-// then row_mirror (lane i <-> 15-i joins the two 8-lane halves of the row).
+// Max over each 16-lane row: group8_max, then row_mirror (lane i <-> 15-i
+// joins the two 8-lane halves of the row).
 __device__ __forceinline__ float group16_max(float v) {
     v = group8_max(v);
     const int x = __float_as_int(v);
     return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false)));
 }
 
-// Max over the 32-lane half-wavefront of a block in the 4-wide lane layout:
-// group8_max, then row_mirror (lane i <-> 15-i: joins the two 8-lane halves
-// of a row), then ds_swizzle in bit mode with xor mask 16 (swaps the two
-// 16-lane rows of each 32-lane group).
+// Max over each 32-lane half-wavefront: group16_max, then ds_swizzle in bit
+// mode with xor mask 16 (swaps the two 16-lane rows of each 32-lane group).
 __device__ __forceinline__ float group32_max(float v) {
     v = group16_max(v);
     const int x = __float_as_int(v);
@@ -120,16 +117,6 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
     return (uint32_t)w;
 }
 
-// codes of fl32(v[j] / s) for a granule; s > 0.  The division is IEEE
-// (correctly rounded, denormals kept), as the quantization rule requires.
-__device__ __forceinline__ uint4 encode16(const float (&v)[kGranule], float s) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        w[j] = encode4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // exact decode of the four codes in a dword
 __device__ __forceinline__ void decode4(uint32_t w, float* out) {
     auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
@@ -140,36 +127,72 @@ __device__ __forceinline__ void decode4(uint32_t w, float* out) {
     out[3] = hi[1];
 }
 
-// d[j] = fl32(E4M3(code j) * s)
-__device__ __forceinline__ void dequant16(uint4 c, float s, float (&d)[kGranule]) {
-    decode4(c.x, d + 0);
-    decode4(c.y, d + 4);
-    decode4(c.z, d + 8);
-    decode4(c.w, d + 12);
-#pragma unroll
-    for (int j = 0; j < kGranule; ++j) d[j] = d[j] * s;
-}
+// ---------------------------------------------------------------------------
+// granule layout (16 elements per lane, 8 lanes per block)
+// ---------------------------------------------------------------------------
 
-// d[j] = fl32(E4M3(code byte j) * s) for the four codes of a dword
-__device__ __forceinline__ void dequant4(uint32_t c, float s, float (&d)[kQuad]) {
-    decode4(c, d);
+// Blockwise quantization of a granule whose 8-lane group forms one block:
+// returns the codes of fl32(v[j] / s) and sets *scale = fl32(absmax / 448)
+// (identical in all 8 lanes).  The divisions are IEEE (correctly rounded,
+// denormals kept), as the quantization rule requires.
+__device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], float* scale) {
+    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kQuad; ++j) d[j] = d[j] * s;
-}
-
-// Blockwise quantization of a quad whose 32-lane group forms one block:
-// returns the four codes and sets *scale (identical in all 32 lanes).
-__device__ __forceinline__ uint32_t quantize_quad(const float (&v)[kQuad], float* scale) {
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    amax = group32_max(amax);
+    for (int j = 0; j < kGranule; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group8_max(amax);
     const float s = amax / kFp8Max;
     *scale = s;
-    if (s == 0.0f) return 0u;
-    return encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    if (s == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = encode4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ---------------------------------------------------------------------------
-// lane vectors of W = 4 or 8 elements
+// bfloat16
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two floats -> two bf16 (round to nearest even) packed low/high
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 ha = (__bf16)a;
+    __bf16 hb = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// granule loads: four 16-byte loads for fp32, two for bf16 (widened exactly)
+__device__ __forceinline__ void load16(const float* __restrict__ p, float (&v)[kGranule]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float4 t = q[j];
+        v[4 * j] = t.x;
+        v[4 * j + 1] = t.y;
+        v[4 * j + 2] = t.z;
+        v[4 * j + 3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&v)[kGranule]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint4 t = q[j];
+        uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[8 * j + 2 * k] = bf16lo(w[k]);
+            v[8 * j + 2 * k + 1] = bf16hi(w[k]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// lane vectors of W = 4 or 8 elements (128/W lanes per block)
 // ---------------------------------------------------------------------------
 
 template <int W> struct LaneCodes;
@@ -201,7 +224,12 @@ __device__ __forceinline__ void store_codes(uint8_t* __restrict__ p, typename La
 }
 
 // d[j] = fl32(E4M3(code j) * s)
-__device__ __forceinline__ void dequant_lane(uint32_t c, float s, float (&d)[4]) { dequant4(c, s, d); }
+__device__ __forceinline__ void dequant_lane(uint32_t c, float s, float (&d)[4]) {
+    decode4(c, d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = d[j] * s;
+}
+
 __device__ __forceinline__ void dequant_lane(uint2 c, float s, float (&d)[8]) {
     decode4(c.x, d);
     decode4(c.y, d + 4);
@@ -211,7 +239,15 @@ __device__ __forceinline__ void dequant_lane(uint2 c, float s, float (&d)[8]) {
 
 // Blockwise quantization of a lane vector whose 128/W-lane group forms one
 // block: returns the codes and sets *scale (identical across the group).
-__device__ __forceinline__ uint32_t quantize_lane(const float (&v)[4], float* scale) { return quantize_quad(v, scale); }
+__device__ __forceinline__ uint32_t quantize_lane(const float (&v)[4], float* scale) {
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = group32_max(amax);
+    const float s = amax / kFp8Max;
+    *scale = s;
+    if (s == 0.0f) return 0u;
+    return encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+}
+
 __device__ __forceinline__ uint2 quantize_lane(const float (&v)[8], float* scale) {
     float amax = 0.0f;
 #pragma unroll
@@ -223,100 +259,16 @@ __device__ __forceinline__ uint2 quantize_lane(const float (&v)[8], float* scale
     return make_uint2(encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s), encode4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
 }
 
-// Blockwise quantization of a granule whose 8-lane group forms one block:
-// returns the codes and sets *scale (identical in all 8 lanes).
-__device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], float* scale) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kGranule; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = group8_max(amax);
-    const float s = amax / kFp8Max;
-    *scale = s;
-    if (s == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
-    return encode16(v, s);
-}
-
-// ---------------------------------------------------------------------------
-// bfloat16
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// two floats -> two bf16 (round to nearest even) packed low/high
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 ha = (__bf16)a;
-    __bf16 hb = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-// ---------------------------------------------------------------------------
-// granule loads / stores
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ void load16(const float* __restrict__ p, float (&v)[kGranule]) {
-    const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float4 t = q[j];
-        v[4 * j] = t.x;
-        v[4 * j + 1] = t.y;
-        v[4 * j + 2] = t.z;
-        v[4 * j + 3] = t.w;
-    }
-}
-
-__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&v)[kGranule]) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        uint4 t = q[j];
-        uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[8 * j + 2 * k] = bf16lo(w[k]);
-            v[8 * j + 2 * k + 1] = bf16hi(w[k]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// quad stores (non-temporal)
-// ---------------------------------------------------------------------------
-
-
-__device__ __forceinline__ void store_quad_nt(float* __restrict__ p, const float (&d)[kQuad]) {
+// 16-byte non-temporal stores of a lane's output (W = 4 fp32, W = 8 bf16)
+__device__ __forceinline__ void store_lane_nt(float* __restrict__ p, const float (&d)[4]) {
     const f32x4_t v = {d[0], d[1], d[2], d[3]};
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
 
-__device__ __forceinline__ void store_quad_nt(uint16_t* __restrict__ p, const float (&d)[kQuad]) {
-    const u32x2_t v = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
-}
-
-// 16-byte non-temporal stores of a lane's output (W = 4 fp32, W = 8 bf16)
-__device__ __forceinline__ void store_lane_nt(float* __restrict__ p, const float (&d)[4]) { store_quad_nt(p, d); }
 __device__ __forceinline__ void store_lane_nt(uint16_t* __restrict__ p, const float (&d)[8]) {
     const u32x4_t v = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]),
                        pack_bf16x2(d[6], d[7])};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void store_lane_nt(uint16_t* __restrict__ p, const float (&d)[4]) { store_quad_nt(p, d); }
-
-__device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[kGranule]) {
-    float4* q = reinterpret_cast<float4*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-}
-
-__device__ __forceinline__ void store16(uint16_t* __restrict__ p, const float (&v)[kGranule]) {
-    uint4* q = reinterpret_cast<uint4*>(p);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        q[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
-                          pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
 }
 
 }  // namespace lpc
