@@ -5,9 +5,9 @@
 // The quantizers use one 16-element granule per lane (a wavefront covers 8
 // scale blocks); the reduce-scatter, all-gather, fused and dequantize kernels
 // give each lane a vector of 4 or 8 elements, so that every lane writes 16
-// bytes (see lpc_device.hpp).  Streaming kernels use 256-lane workgroups.  Rank loops are
-// unrolled by template parameter so that all N loads of a lane are in flight
-// before the first add.
+// bytes (see lpc_device.hpp).  Streaming kernels use 256-lane workgroups.
+// Rank loops are unrolled by template parameter so that all N loads of a lane
+// are in flight before the first add.
 #include "lpc_device.hpp"
 #include "lpc_launch.hpp"
 

@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lpc.h")
 
 BLOCK = 128
 MAX_RANKS = 8
+MAX_ELEMS = 1 << 32
 LPC_F32, LPC_BF16 = 0, 1
 ALGO_AUTO, ALGO_DDA_FLAT, ALGO_DDA_TREE, ALGO_LOW_PRECISION = 0, 1, 2, 3
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DDA_FLAT: "dda_flat", ALGO_DDA_TREE: "dda_tree",

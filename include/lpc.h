@@ -79,8 +79,11 @@ typedef enum {
     LPC_BF16 = 1        /* bfloat16 bit patterns (uint16) */
 } lpc_dtype;
 
-/* Largest element count accepted by any call (keeps every index in range). */
-#define LPC_MAX_ELEMS ((size_t)1 << 38)
+/* Largest element count accepted by any call: 2^32 elements (16 GiB of fp32).
+ * The narrowest kernels give each lane 4 elements, and HIP takes at most
+ * 2^31 - 1 lanes along a grid dimension, so every launch stays within that
+ * limit; larger buffers go in several calls. */
+#define LPC_MAX_ELEMS ((size_t)1 << 32)
 
 /* ---------------------------------------------------------------------- */
 /* Low-precision AllReduce, one rank's steps                               */

@@ -17,6 +17,7 @@ OK, NULL, SHAPE, RANKS, DTYPE, ALIGN, HIP = range(7)
 A = 0x10000        # a fake 16-byte-aligned device address
 B = 0x10008        # a fake misaligned one
 F32, BF16 = 0, 1
+MAX_ELEMS = lpc.MAX_ELEMS
 
 
 @pytest.fixture(scope="module")
@@ -33,6 +34,14 @@ def L():
 
 def arr(*ptrs):
     return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def test_header_limits_match_binding():
+    text = open(lpc.HEADER).read()
+    assert re.search(r"#define LPC_MAX_ELEMS \(\(size_t\)1 << (\d+)\)", text).group(1) == "32"
+    # the narrowest kernels take 4 elements per lane; HIP accepts at most
+    # 2^31 - 1 lanes along one grid dimension
+    assert MAX_ELEMS // 4 < 2 ** 31
 
 
 def test_exports_every_declared_function(L):
@@ -66,7 +75,7 @@ def test_quantize_errors(L):
     assert f(A, F32, 128, A, A + 4, None) == ALIGN
     assert f(A, F32, 100, A, A, None) == SHAPE
     assert f(A, F32, 129, A, A, None) == SHAPE
-    assert f(A, F32, (1 << 38) + 128, A, A, None) == SHAPE
+    assert f(A, F32, MAX_ELEMS + 128, A, A, None) == SHAPE
 
 
 @pytest.mark.parametrize("name", ["lpc_reduce_scatter_chunk"])
@@ -130,7 +139,7 @@ def test_dda_errors(L):
     assert f(arr(A, A), 2, 0, None, None) == OK
     assert f(arr(A, None), 2, 16, A, None) == NULL
     assert f(arr(A, B), 2, 16, A, None) == ALIGN
-    assert f(arr(A, A), 2, (1 << 38) + 1, A, None) == SHAPE
+    assert f(arr(A, A), 2, MAX_ELEMS + 1, A, None) == SHAPE
     g = L.dda_tree_reduce_scatter
     assert g(arr(A, A), 9, 2, 0, 32, A, None) == DTYPE
     assert g(arr(A, A), F32, 2, 3, 32, A, None) == RANKS
