@@ -46,6 +46,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,12 +93,17 @@ KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every kernel's device
 
 
 def source_digest() -> str:
-    """Digest of the kernels' device sources (the counters in profiles/ are valid for it)."""
+    """Digest of the kernels' device sources (the counters in profiles/ are valid for
+    it).  Comments and whitespace are left out, so that only a change to the code
+    itself invalidates the counters."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_precision_allreduce_amd", "csrc")
     for f in KERNEL_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update((f + " " + " ".join(text.split())).encode())
     return h.hexdigest()[:16]
 
 
