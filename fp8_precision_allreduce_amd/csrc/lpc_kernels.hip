@@ -471,137 +471,294 @@ hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size
 }
 
 // ---------------------------------------------------------------------------
-// all-to-all-v routing: one workgroup of 1024 lanes (16 wavefronts).  Rows are
-// taken in super-tiles of 16 x 1024: lane t holds rows st + b*1024 + t,
-// b = 0..15, in registers (one batch of loads, then no global reads), so a
-// super-tile costs one load latency.
-//   pass 1: per-destination counts, from wavefront ballots; counts, and
-//           offsets as their exclusive prefix.
-//   pass 2: for each super-tile, the ballots give every row its rank among
-//           the earlier lanes of its wavefront with the same destination, and
-//           every (b, wavefront) its count per destination; an exclusive
-//           prefix over (b, wavefront) in row order, started at the
-//           destination's running base, places each row: a stable,
-//           destination-major permutation.
+// all-to-all-v routing.  Row k with destination j goes to packed position
+// offsets[j] + (number of rows before k with destination j): a stable,
+// destination-major permutation.
+//
+// Workgroup w places the rows of its own tile [w*T, (w+1)*T) and needs, for
+// that, the per-destination counts of all rows (for the offsets) and of the
+// rows before its tile.  There is no scratch memory through which workgroups
+// could share partial counts, so every workgroup counts the whole destination
+// array itself: 4 bytes a row, re-read from L2, and a handful of VALU
+// operations per row, against a placement pass that would otherwise run on
+// one CU.  The number of workgroups is capped, which bounds the re-reading.
+//   counting  a lane loads 4 rows with one 16-byte load, 16 sub-tiles at a
+//             time; a row adds one to its destination's byte of a 64-bit
+//             per-lane counter, folded into 32-bit counters before a byte can
+//             overflow; then a workgroup-wide sum.
+//   placing   1024 rows at a time, 4 contiguous rows per lane: each lane
+//             counts its rows per destination in eight 16-bit fields, an
+//             exclusive scan over the lanes gives each row the number of
+//             earlier rows of its destination in the sub-tile, and the
+//             destination's running base (kept in every lane's registers)
+//             adds the rest.  The first sub-tile is loaded and scanned
+//             together with the counting, so a tile of one sub-tile needs a
+//             single barrier.
+// Rows with an out-of-range destination are dropped; the workgroups fill the
+// part of perm past the last placed row with -1.
 // ---------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kRouteBatch = 16;
-constexpr size_t kRouteSuperTile = (size_t)kRouteBatch * kRouteThreads;
+constexpr int kRouteRowsPerLane = 4;
+constexpr size_t kRouteSubTile = (size_t)kRouteThreads * kRouteRowsPerLane;  // 1024 rows
+constexpr int kRouteUnroll = 16;            // sub-tiles in flight per lane while counting
+constexpr size_t kRouteMaxGroups = 128;
 
-// number of lanes below this one whose bit is set in mask
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+// Sum over the wavefront, in every lane: DPP inside each 16-lane row (xor 1,
+// xor 2, half-row mirror, row mirror), then the four row sums via readlane.
+// Needs all 64 lanes active.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);
+    return (uint32_t)(__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+                      __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
 }
 
-__device__ __forceinline__ void load_route_batch(const int32_t* __restrict__ dest, size_t rows, size_t st,
-                                                 int nranks, int32_t (&d)[kRouteBatch]) {
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-        const size_t k = st + (size_t)b * kRouteThreads + threadIdx.x;
-        const int32_t v = k < rows ? dest[k] : -1;
-        d[b] = (v >= 0 && v < nranks) ? v : -1;  // out-of-range destinations are dropped
+// Inclusive prefix sum over the lanes of the wavefront: row_shr 1, 2, 4, 8
+// inside each 16-lane row (a lane with no source lane in its row adds 0), then
+// the totals of the rows below, via readlane.  Needs all 64 lanes active.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+    return (uint32_t)x;
+}
+
+// rows k .. k+3 of dest (k % 4 == 0), -1 for a row at or past `end`
+__device__ __forceinline__ int4 load_raw4(const int32_t* __restrict__ dest, size_t end, size_t k) {
+    int4 v = make_int4(-1, -1, -1, -1);
+    if (k + 4 <= end) {
+        v = *reinterpret_cast<const int4*>(dest + k);
+    } else {
+        if (k < end) v.x = dest[k];
+        if (k + 1 < end) v.y = dest[k + 1];
+        if (k + 2 < end) v.z = dest[k + 2];
     }
+    return v;
+}
+
+// one in byte d of a 64-bit counter for a destination d in [0, nranks),
+// nothing for any other value
+__device__ __forceinline__ uint64_t dest_byte(int32_t d, int nranks) {
+    return (uint64_t)((uint32_t)d < (uint32_t)nranks ? 1u : 0u) << ((d & 7) * 8);
+}
+
+// This lane's per-destination counts of the rows before row `split` and of
+// the rest (split % 1024 == 0).  The lane reads rows 4*t + 1024*u, 16
+// sub-tiles per round with all 16 loads in flight (rows past the end read as
+// -1); a sub-tile lies wholly on one side of `split`.
+__device__ __forceinline__ void count_rows(const int32_t* __restrict__ dest, size_t rows, int nranks,
+                                           size_t split, uint32_t (&before)[kMaxRanks],
+                                           uint32_t (&after)[kMaxRanks]) {
+    for (size_t s0 = 0; s0 < rows; s0 += kRouteUnroll * kRouteSubTile) {
+        int4 v[kRouteUnroll];
+#pragma unroll
+        for (int u = 0; u < kRouteUnroll; ++u)
+            v[u] = load_raw4(dest, rows, s0 + u * kRouteSubTile + (size_t)kRouteRowsPerLane * threadIdx.x);
+        uint64_t lo = 0, hi = 0;  // at most 64 per byte
+#pragma unroll
+        for (int u = 0; u < kRouteUnroll; ++u) {
+            const uint64_t b = dest_byte(v[u].x, nranks) + dest_byte(v[u].y, nranks) + dest_byte(v[u].z, nranks) +
+                               dest_byte(v[u].w, nranks);
+            if (s0 + u * kRouteSubTile < split)
+                lo += b;
+            else
+                hi += b;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxRanks; ++j) {
+            before[j] += (uint32_t)(lo >> (8 * j)) & 0xFFu;
+            after[j] += (uint32_t)(hi >> (8 * j)) & 0xFFu;
+        }
+    }
+}
+
+// 16-bit field d & 7 of four packed registers (destinations 2r, 2r+1 in
+// register r).  The registers are paired into 64-bit values before the
+// select: a select between array elements would be folded into an indexed
+// load, and the array moved out of registers.
+__device__ __forceinline__ uint32_t field16(const uint32_t (&f)[4], int32_t d) {
+    const uint64_t lo = ((uint64_t)f[1] << 32) | f[0], hi = ((uint64_t)f[3] << 32) | f[2];
+    const uint64_t x = (d & 4) ? hi : lo;
+    return (uint32_t)(x >> ((d & 3) * 16)) & 0xFFFFu;
+}
+
+// v[d & 7], selected the same way
+__device__ __forceinline__ uint32_t pick8(const uint32_t (&v)[kMaxRanks], int32_t d) {
+    const uint64_t p01 = ((uint64_t)v[1] << 32) | v[0], p23 = ((uint64_t)v[3] << 32) | v[2];
+    const uint64_t p45 = ((uint64_t)v[5] << 32) | v[4], p67 = ((uint64_t)v[7] << 32) | v[6];
+    const uint64_t x = (d & 4) ? ((d & 2) ? p67 : p45) : ((d & 2) ? p23 : p01);
+    return (uint32_t)(x >> ((d & 1) * 32));
+}
+
+// The lane's per-destination row counts (at most 4 each) as eight 16-bit
+// fields in four registers: destinations 2r and 2r+1 in register r.
+__device__ __forceinline__ void lane_fields(const int32_t (&d)[kRouteRowsPerLane], int nranks, uint32_t (&own)[4]) {
+    uint64_t bytes = 0;
+#pragma unroll
+    for (int i = 0; i < kRouteRowsPerLane; ++i) bytes += dest_byte(d[i], nranks);
+    const uint32_t lo = (uint32_t)bytes, hi = (uint32_t)(bytes >> 32);
+    own[0] = (lo & 0xFFu) | ((lo << 8) & 0xFF0000u);
+    own[1] = ((lo >> 16) & 0xFFu) | ((lo >> 8) & 0xFF0000u);
+    own[2] = (hi & 0xFFu) | ((hi << 8) & 0xFF0000u);
+    own[3] = ((hi >> 16) & 0xFFu) | ((hi >> 8) & 0xFF0000u);
+}
+
+// Scatter this lane's rows k .. k+3 of a sub-tile.  excl: the fields of the
+// rows of its destinations in earlier lanes of the sub-tile; base: each
+// destination's packed position of the sub-tile's first such row.
+__device__ __forceinline__ void place_rows(const int32_t (&d)[kRouteRowsPerLane], int nranks, size_t k,
+                                           const uint32_t (&excl)[4], const uint32_t (&base)[kMaxRanks],
+                                           int32_t* __restrict__ perm) {
+    uint32_t pos[kRouteRowsPerLane];
+#pragma unroll
+    for (int i = 0; i < kRouteRowsPerLane; ++i) {
+        uint32_t same = 0;  // earlier rows of this lane with the same destination
+#pragma unroll
+        for (int e = 0; e < i; ++e) same += d[e] == d[i] ? 1u : 0u;
+        pos[i] = pick8(base, d[i]) + field16(excl, d[i]) + same;
+    }
+#pragma unroll
+    for (int i = 0; i < kRouteRowsPerLane; ++i)
+        if ((uint32_t)d[i] < (uint32_t)nranks) perm[pos[i]] = (int32_t)(k + i);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t* __restrict__ dest,
-                                                                   size_t rows, int nranks,
+                                                                   size_t rows, int nranks, size_t tile,
                                                                    int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ perm) {
-    __shared__ int32_t wave_cnt[kRouteBatch][kRouteWaves][kMaxRanks];  // then the in-batch prefix
-    __shared__ int32_t batch_base[kRouteBatch][kMaxRanks];
-    __shared__ int32_t base[kMaxRanks];
-    __shared__ int32_t placed;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int32_t d[kRouteBatch];
+    __shared__ uint32_t wave_part[kRouteWaves][2 * kMaxRanks];
+    __shared__ uint32_t wave_tot[kRouteWaves][4];
+    const int t = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wavefront index, kept scalar
+    const size_t ts = (size_t)blockIdx.x * tile;
+    const size_t te = ts + tile < rows ? ts + tile : rows;
 
-    // pass 1: counts
-    int32_t cnt[kMaxRanks];
+    // The first sub-tile of this workgroup's rows is loaded with the counting
+    // loads and scanned with the counts, so that one barrier serves both.
+    size_t k = ts + (size_t)kRouteRowsPerLane * t;
+    const int4 first = load_raw4(dest, te, k);
+    uint32_t before[kMaxRanks], after[kMaxRanks];
 #pragma unroll
-    for (int j = 0; j < kMaxRanks; ++j) cnt[j] = 0;
-    for (size_t st = 0; st < rows; st += kRouteSuperTile) {
-        load_route_batch(dest, rows, st, nranks, d);
+    for (int j = 0; j < kMaxRanks; ++j) before[j] = after[j] = 0;
+    count_rows(dest, rows, nranks, ts, before, after);
+
+    int32_t d[kRouteRowsPerLane] = {first.x, first.y, first.z, first.w};
+    uint32_t own[4], excl[4];
+    lane_fields(d, nranks, own);
 #pragma unroll
-        for (int b = 0; b < kRouteBatch; ++b)
-#pragma unroll
-            for (int j = 0; j < kMaxRanks; ++j) cnt[j] += __popcll(__ballot(d[b] == j));
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t incl = wave_scan(own[r]);
+        excl[r] = incl - own[r];
+        if ((t & 63) == 63) wave_tot[w][r] = incl;
     }
-    if (lane == 0) {
 #pragma unroll
-        for (int j = 0; j < kMaxRanks; ++j) wave_cnt[0][w][j] = cnt[j];
+    for (int j = 0; j < kMaxRanks; ++j) {
+        const uint32_t b = wave_sum(before[j]), a = wave_sum(after[j]);
+        if ((t & 63) == 0) {
+            wave_part[w][j] = b;
+            wave_part[w][kMaxRanks + j] = a;
+        }
     }
     __syncthreads();
-    if (t == 0) {
-        int32_t acc = 0;
+
+    // every lane: totals, offsets and the bases of this tile's first
+    // sub-tile (destinations at or past nranks count zero rows)
+    uint32_t bef[kMaxRanks], tot[kMaxRanks];
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+        bef[j] = tot[j] = 0;
+#pragma unroll
+        for (int v = 0; v < kRouteWaves; ++v) {
+            bef[j] += wave_part[v][j];
+            tot[j] += wave_part[v][kMaxRanks + j];
+        }
+        tot[j] += bef[j];
+    }
+    uint32_t base[kMaxRanks], off[kMaxRanks], placed = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+        off[j] = placed;
+        base[j] = placed + bef[j];
+        placed += tot[j];
+    }
+    if (blockIdx.x == 0 && t == 0) {
+#pragma unroll
         for (int j = 0; j < kMaxRanks; ++j) {
-            int32_t c = 0;
-            for (int v = 0; v < kRouteWaves; ++v) c += wave_cnt[0][v][j];
-            base[j] = acc;
             if (j < nranks) {
-                counts[j] = c;
-                offsets[j] = acc;
-                acc += c;
+                counts[j] = (int32_t)tot[j];
+                offsets[j] = (int32_t)off[j];
             }
         }
-        placed = acc;
     }
-    __syncthreads();
 
-    // pass 2: stable scatter, one super-tile at a time
-    for (size_t st = 0; st < rows; st += kRouteSuperTile) {
-        load_route_batch(dest, rows, st, nranks, d);
-        int32_t rank_in_wave[kRouteBatch];
+    for (size_t s = ts;;) {
+        uint32_t sub[4];  // the sub-tile's fields, all lanes
 #pragma unroll
-        for (int b = 0; b < kRouteBatch; ++b) {
-            rank_in_wave[b] = 0;
+        for (int r = 0; r < 4; ++r) {
+            sub[r] = 0;
 #pragma unroll
-            for (int j = 0; j < kMaxRanks; ++j) {
-                const uint64_t m = __ballot(d[b] == j);
-                if (d[b] == j) rank_in_wave[b] = lanes_below(m);
-                if (lane == 0) wave_cnt[b][w][j] = __popcll(m);
-            }
-        }
-        __syncthreads();
-        if (t < kRouteBatch * kMaxRanks) {  // (b, j): exclusive prefix over the wavefronts of batch b
-            const int b = t / kMaxRanks, j = t % kMaxRanks;
-            int32_t run = 0;
             for (int v = 0; v < kRouteWaves; ++v) {
-                const int32_t c = wave_cnt[b][v][j];
-                wave_cnt[b][v][j] = run;
-                run += c;
+                const uint32_t c = wave_tot[v][r];
+                excl[r] += v < w ? c : 0u;
+                sub[r] += c;
             }
-            batch_base[b][j] = run;
         }
-        __syncthreads();
-        if (t < kMaxRanks) {  // j: exclusive prefix over the batches, from the running base
-            int32_t run = base[t];
-            for (int b = 0; b < kRouteBatch; ++b) {
-                const int32_t c = batch_base[b][t];
-                batch_base[b][t] = run;
-                run += c;
-            }
-            base[t] = run;
-        }
-        __syncthreads();
+        place_rows(d, nranks, k, excl, base, perm);
+        s += kRouteSubTile;
+        if (s >= te) break;
 #pragma unroll
-        for (int b = 0; b < kRouteBatch; ++b) {
-            if (d[b] >= 0) {
-                const size_t k = st + (size_t)b * kRouteThreads + t;
-                perm[batch_base[b][d[b]] + wave_cnt[b][w][d[b]] + rank_in_wave[b]] = (int32_t)k;
-            }
+        for (int j = 0; j < kMaxRanks; ++j) base[j] += field16(sub, j);
+        // the next sub-tile (tiles of more than 1024 rows only)
+        k = s + (size_t)kRouteRowsPerLane * t;
+        const int4 next = load_raw4(dest, te, k);
+        d[0] = next.x;
+        d[1] = next.y;
+        d[2] = next.z;
+        d[3] = next.w;
+        lane_fields(d, nranks, own);
+        __syncthreads();  // every lane has read wave_tot
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t incl = wave_scan(own[r]);
+            excl[r] = incl - own[r];
+            if ((t & 63) == 63) wave_tot[w][r] = incl;
         }
-        __syncthreads();  // the next super-tile rewrites wave_cnt and batch_base
+        __syncthreads();
     }
-    // rows with an out-of-range destination were dropped: mark perm's tail
-    for (size_t k = (size_t)placed + t; k < rows; k += kRouteThreads) perm[k] = -1;
+
+    // the tail of perm past the placed rows
+    const size_t q0 = placed > ts ? placed : ts;
+    for (size_t q = q0 + t; q < te; q += kRouteThreads) perm[q] = -1;
+}
+
+// Workgroups and tile size: one 1024-row sub-tile per workgroup up to
+// kRouteMaxGroups workgroups, larger tiles (whole sub-tiles) beyond.
+static void route_tiles(size_t rows, size_t* groups, size_t* tile) {
+    const size_t subtiles = (rows + kRouteSubTile - 1) / kRouteSubTile;
+    const size_t g = subtiles < kRouteMaxGroups ? subtiles : kRouteMaxGroups;
+    *tile = (subtiles + g - 1) / g * kRouteSubTile;
+    *groups = (rows + *tile - 1) / *tile;
 }
 
 hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32_t* counts, int32_t* offsets,
                              int32_t* perm, hipStream_t stream) {
-    launch(a2av_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, dest, rows, nranks, counts,
-           offsets, perm);
+    size_t groups, tile;
+    route_tiles(rows, &groups, &tile);
+    launch(a2av_route_kernel, dim3((unsigned)groups), dim3(kRouteThreads), 0, stream, dest, rows, nranks, tile,
+           counts, offsets, perm);
     return hipGetLastError();
 }
 

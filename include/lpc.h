@@ -192,7 +192,8 @@ lpc_status dda_tree_allgather(const void *const chunks[], lpc_dtype t, int nrank
  *              order kept within a destination (stable)
  * Rows with an out-of-range destination are dropped: they are not counted
  * and perm's tail past sum(counts) is filled with -1.
- *   rows < 2^31.  One workgroup; result ready when the stream reaches it.    */
+ *   rows < 2^31.  Each workgroup places one tile of rows and counts the
+ *   whole of `dest` itself (no scratch memory), up to 128 workgroups.  */
 lpc_status lpc_a2av_route(const int32_t *dest, size_t rows, int nranks,
                           int32_t *counts, int32_t *offsets, int32_t *perm,
                           hipStream_t stream);

@@ -451,7 +451,10 @@ def test_dda_tree(dev, orc, bf16):
 # -- all-to-all-v ----------------------------------------------------------------------------------
 
 def test_a2av_route_cfg5(dev, orc):
-    for rows, nranks in ((inputs.A2AV_ROWS, 8), (1, 8), (1000, 3), (70_000, 8)):
+    # one workgroup per 1024-row sub-tile up to 128 workgroups, then larger
+    # tiles: sizes around a sub-tile, ragged tails and multi-sub-tile tiles
+    for rows, nranks in ((inputs.A2AV_ROWS, 8), (1, 8), (1000, 3), (1023, 8), (1024, 8), (1025, 5),
+                         (4097, 1), (70_000, 8), (140_000, 7), (300_001, 8)):
         dest = inputs.zipf_destinations(rows=rows, nranks=nranks)
         say("a2av route rows=%d nranks=%d" % (rows, nranks))
         counts = torch.empty(nranks, dtype=torch.int32, device=dev)
@@ -474,6 +477,28 @@ def test_a2av_route_drops_bad_destinations(dev):
     assert to_host(counts).tolist() == [2, 0, 0, 1, 0, 0, 0, 1]
     assert to_host(offsets).tolist() == [0, 2, 2, 2, 3, 3, 3, 3]
     assert to_host(perm).tolist() == [2, 5, 0, 4, -1, -1]
+
+
+def test_a2av_route_drops_bad_destinations_large(dev, orc):
+    """Out-of-range destinations spread over many workgroups: the valid rows are
+    routed as the oracle routes them alone, and perm's tail is -1."""
+    rng = np.random.default_rng(11)
+    for rows, bad in ((5000, 0.15), (140_000, 0.02), (3000, 1.0)):
+        dest = inputs.zipf_destinations(rows=rows, nranks=8).copy()
+        hit = rng.random(rows) < bad
+        dest[hit] = np.where(rng.random(int(hit.sum())) < 0.5, -1, 8 + rng.integers(0, 5, int(hit.sum())))
+        say("a2av route rows=%d with %d out-of-range destinations" % (rows, int(hit.sum())))
+        counts = torch.empty(8, dtype=torch.int32, device=dev)
+        offsets = torch.empty(8, dtype=torch.int32, device=dev)
+        perm = torch.empty(rows, dtype=torch.int32, device=dev)
+        lpc.lpc_a2av_route(to_dev(dest, dev), 8, counts, offsets, perm)
+        keep = np.nonzero(~hit)[0].astype(np.int32)
+        rc, ro, rp = orc.a2av_route(dest[keep], 8) if keep.size else (np.zeros(8, np.int32),) * 2 + (keep,)
+        want = np.full(rows, -1, np.int32)
+        want[:keep.size] = keep[rp]
+        assert_same(to_host(counts), rc, "counts")
+        assert_same(to_host(offsets), ro, "offsets")
+        assert_same(to_host(perm), want, "perm")
 
 
 def test_a2av_quantize_rows_small(dev, orc):
