@@ -117,6 +117,42 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
     return (uint32_t)w;
 }
 
+// Blocks whose scale is at least this take the reciprocal route below; the
+// rest divide.  It keeps every residual and quotient that can change a code
+// clear of underflow.
+constexpr float kMinRecipScale = 0x1p-80f;
+
+// fl32(v / s), the correctly rounded quotient, from r = fl32(1 / s): q0 =
+// fl32(v * r) is within 1.5 ulp of v / s; a correction step q + fl32(v - q*s)
+// * r (two FMAs, the residual exact) brings it within one ulp, and a second
+// step then gives the correctly rounded quotient (Markstein's theorem: with r
+// within half an ulp of 1/s and q within one ulp of v/s, the corrected
+// quotient is v/s rounded to nearest).  The sign is copied from v so that -0
+// stays -0.  Quotients below 2^-10 in magnitude, the only ones an underflow
+// could touch when s >= kMinRecipScale, encode as signed zero either way.
+__device__ __forceinline__ float quotient(float v, float s, float r) {
+    const float q0 = v * r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, v), r, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, s, v), r, q1);
+    return __builtin_copysignf(q2, v);
+}
+
+// codes of fl32(v[j] / s), four per dword, for a block scale s > 0
+template <int N>
+__device__ __forceinline__ void encode_quotients(const float (&v)[N], float s, uint32_t (&w)[N / 4]) {
+    float q[N];
+    if (s >= kMinRecipScale) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int j = 0; j < N; ++j) q[j] = quotient(v[j], s, r);
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) q[j] = v[j] / s;
+    }
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) w[k] = encode4(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
+}
+
 // exact decode of the four codes in a dword
 __device__ __forceinline__ void decode4(uint32_t w, float* out) {
     auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
@@ -133,8 +169,8 @@ __device__ __forceinline__ void decode4(uint32_t w, float* out) {
 
 // Blockwise quantization of a granule whose 8-lane group forms one block:
 // returns the codes of fl32(v[j] / s) and sets *scale = fl32(absmax / 448)
-// (identical in all 8 lanes).  The divisions are IEEE (correctly rounded,
-// denormals kept), as the quantization rule requires.
+// (identical in all 8 lanes).  The scale is an IEEE division; the quotients
+// are correctly rounded (quotient()), as the quantization rule requires.
 __device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], float* scale) {
     float amax = 0.0f;
 #pragma unroll
@@ -144,8 +180,7 @@ __device__ __forceinline__ uint4 quantize_granule(const float (&v)[kGranule], fl
     *scale = s;
     if (s == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
     uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = encode4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+    encode_quotients(v, s, w);
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -245,7 +280,9 @@ __device__ __forceinline__ uint32_t quantize_lane(const float (&v)[4], float* sc
     const float s = amax / kFp8Max;
     *scale = s;
     if (s == 0.0f) return 0u;
-    return encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    uint32_t w[1];
+    encode_quotients(v, s, w);
+    return w[0];
 }
 
 __device__ __forceinline__ uint2 quantize_lane(const float (&v)[8], float* scale) {
@@ -256,7 +293,9 @@ __device__ __forceinline__ uint2 quantize_lane(const float (&v)[8], float* scale
     const float s = amax / kFp8Max;
     *scale = s;
     if (s == 0.0f) return make_uint2(0u, 0u);
-    return make_uint2(encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s), encode4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
+    uint32_t w[2];
+    encode_quotients(v, s, w);
+    return make_uint2(w[0], w[1]);
 }
 
 // 16-byte non-temporal stores of a lane's output (W = 4 fp32, W = 8 bf16)

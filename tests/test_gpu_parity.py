@@ -204,6 +204,60 @@ def test_quantize_matches_oracle(dev, orc, bf16):
         assert_same(to_host(scales), rs, name + " scales")
 
 
+def _bf16_blocks(amax_bits: int) -> np.ndarray:
+    """Every finite bf16 value v with |v| <= amax (both signs), 127 to a block,
+    each block led by amax itself so that all blocks share one scale."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    amax = np.float32((np.uint32(amax_bits) << 16).view(np.float32))
+    keep = vals[np.isfinite(vals) & (np.abs(vals) <= amax)]
+    pad = (-keep.size) % (BLOCK - 1)
+    keep = np.concatenate([keep, np.zeros(pad, np.float32)]).reshape(-1, BLOCK - 1)
+    return np.concatenate([np.full((keep.shape[0], 1), amax, np.float32), keep], axis=1).reshape(-1)
+
+
+# block maxima: tiny; scales just below, at and just above 2^-80, the smallest
+# scale the kernels' reciprocal quotient serves (amax = 1.75 * 2^-72 gives
+# exactly 2^-80); ordinary; large; the largest finite bf16
+_AMAX_BF16 = [0x0200, 0x1BDF, 0x1BE0, 0x1BE1, 0x1C40, 0x2A00, 0x3DCD, 0x3F80, 0x3FC0, 0x4040, 0x43E0,
+              0x5F01, 0x7F7F]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_quantize_every_bf16_value(dev, orc, bf16):
+    """Every bf16 value under a range of block maxima, through the bf16 and the fp32
+    input paths: bf16 quotients often fall exactly on E4M3 rounding midpoints."""
+    x = np.concatenate([_bf16_blocks(a) for a in _AMAX_BF16])
+    say("quantize every bf16 value", "bf16" if bf16 else "f32", x.size)
+    xin = inputs.truncate_to_bf16(x) if bf16 else x
+    codes, scales = gpu_quantize(to_dev(xin, dev))
+    rc, rs = orc.quantize(xin, bf16=bf16)
+    assert_same(to_host(scales), rs, "scales")
+    assert_same(to_host(codes), rc, "codes")
+
+
+def test_quantize_near_midpoints(dev, orc):
+    """fp32 blocks whose quotients land on and within 12 ulps of E4M3 rounding
+    midpoints, at scales from 2^-90 to 2^100 (both sides of 2^-80)."""
+    g = np.random.Generator(np.random.PCG64(107))
+    table = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = ((table[:-1] + table[1:]) / 2).astype(np.float32)
+    nblk = 4096
+    exps = np.concatenate([g.integers(-90, 100, nblk - 512), g.integers(-83, -77, 512)])
+    s = np.ldexp(1.0 + g.integers(0, 1 << 23, nblk) / float(1 << 23), exps).astype(np.float32)
+    q = mids[g.integers(0, mids.size, (nblk, BLOCK))]
+    q = (f32bits(q).astype(np.int64) + g.integers(-12, 13, (nblk, BLOCK))).astype(np.uint32).view(np.float32)
+    q = np.where(g.random((nblk, BLOCK)) < 0.5, -q, q)
+    x = (q.astype(np.float64) * s[:, None]).astype(np.float32)
+    x[:, 0] = (np.float64(448.0) * s).astype(np.float32)
+    x = x.reshape(-1)
+    say("quantize near midpoints", x.size)
+    codes, scales = gpu_quantize(to_dev(x, dev))
+    rc, rs = orc.quantize(x)
+    assert_same(to_host(scales), rs, "scales")
+    assert_same(to_host(codes), rc, "codes")
+
+
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_dequantize_matches_oracle(dev, orc, bf16):
     x = np.concatenate([inputs.rank_buffer(1, 3, 41 * BLOCK), _edge_blocks()])
