@@ -8,6 +8,8 @@
 // bytes (see lpc_device.hpp).  Streaming kernels use 256-lane workgroups.
 // Rank loops are unrolled by template parameter so that all N loads of a lane
 // are in flight before the first add.
+#include <tuple>
+
 #include "lpc_device.hpp"
 #include "lpc_launch.hpp"
 
@@ -24,10 +26,20 @@ __device__ __forceinline__ size_t granule_id() {
     return (size_t)blockIdx.x * kThreads + threadIdx.x;
 }
 
-// Every kernel of the library is launched through this helper.
-template <typename K, typename... Args>
-static void launch(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream, Args... args) {
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+// Every kernel of the library is launched through this helper.  It converts
+// the arguments to the kernel's parameter types and returns the status of
+// this launch itself (not whatever error an earlier call left behind).
+template <typename... P, typename... A>
+static hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream,
+                         A... args) {
+    static_assert(sizeof...(P) == sizeof...(A) && sizeof...(P) > 0, "argument count");
+    std::tuple<P...> vals(args...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+        },
+        vals);
 }
 
 // ---------------------------------------------------------------------------
@@ -53,12 +65,10 @@ hipError_t launch_quantize(const void* x, int in_bf16, size_t n, uint8_t* codes,
                            hipStream_t stream) {
     const size_t ngran = n / kGranule;
     if (in_bf16)
-        launch(quantize_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t*>(x), ngran, codes, scales);
-    else
-        launch(quantize_kernel<float>, grid_for(ngran), dim3(kThreads), 0, stream,
-                           static_cast<const float*>(x), ngran, codes, scales);
-    return hipGetLastError();
+        return launch(quantize_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream,
+                      static_cast<const uint16_t*>(x), ngran, codes, scales);
+    return launch(quantize_kernel<float>, grid_for(ngran), dim3(kThreads), 0, stream, static_cast<const float*>(x),
+                  ngran, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,36 +143,30 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RankCodes in, 
 }
 
 template <int Mode>
-static void launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_t C, uint8_t* cc, float* cs,
-                        void* out, hipStream_t stream) {
+static hipError_t launch_rs_n(const RankCodes& in, int nranks, size_t chunk_off, size_t C, uint8_t* cc, float* cs,
+                              void* out, hipStream_t stream) {
     const dim3 grid = lane_grid<rs_width<Mode>()>(C), block(kThreads);
     switch (nranks) {
-#define LPC_RS_CASE(NR)                                                                              \
-    case NR:                                                                                         \
-        launch((reduce_scatter_kernel<NR, Mode>), grid, block, 0, stream, in, chunk_off, C, cc, cs,  \
-               out);                                                                                 \
-        break;
+#define LPC_RS_CASE(NR) \
+    case NR: return launch(reduce_scatter_kernel<NR, Mode>, grid, block, 0, stream, in, chunk_off, C, cc, cs, out);
         LPC_RS_CASE(1) LPC_RS_CASE(2) LPC_RS_CASE(3) LPC_RS_CASE(4)
         LPC_RS_CASE(5) LPC_RS_CASE(6) LPC_RS_CASE(7) LPC_RS_CASE(8)
 #undef LPC_RS_CASE
     }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_reduce_scatter_chunk(const RankCodes& in, int nranks, int rank, size_t n,
                                        uint8_t* cc, float* cs, hipStream_t stream) {
     const size_t C = n / nranks;
-    launch_rs_n<kRequant>(in, nranks, (size_t)rank * C, C, cc, cs, nullptr, stream);
-    return hipGetLastError();
+    return launch_rs_n<kRequant>(in, nranks, (size_t)rank * C, C, cc, cs, nullptr, stream);
 }
 
 hipError_t launch_reduce_scatter_out(const RankCodes& in, int nranks, int rank, size_t n, void* out,
                                      int out_bf16, hipStream_t stream) {
     const size_t C = n / nranks;
-    if (out_bf16)
-        launch_rs_n<kSumBF16>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
-    else
-        launch_rs_n<kSumF32>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
-    return hipGetLastError();
+    if (out_bf16) return launch_rs_n<kSumBF16>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
+    return launch_rs_n<kSumF32>(in, nranks, (size_t)rank * C, C, nullptr, nullptr, out, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,12 +189,10 @@ hipError_t launch_allgather(const RankCodes& chunks, int nranks, size_t n, void*
                             hipStream_t stream) {
     const size_t C = n / nranks;
     if (out_bf16)
-        launch(allgather_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(C, nranks), dim3(kThreads), 0,
-               stream, chunks, C, static_cast<uint16_t*>(out));
-    else
-        launch(allgather_kernel<float>, lane_grid<lane_width<float>()>(C, nranks), dim3(kThreads), 0, stream,
-               chunks, C, static_cast<float*>(out));
-    return hipGetLastError();
+        return launch(allgather_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(C, nranks), dim3(kThreads), 0,
+                      stream, chunks, C, static_cast<uint16_t*>(out));
+    return launch(allgather_kernel<float>, lane_grid<lane_width<float>()>(C, nranks), dim3(kThreads), 0, stream,
+                  chunks, C, static_cast<float*>(out));
 }
 
 template <typename Out>
@@ -208,12 +210,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, void* out, int out_bf16,
                           hipStream_t stream) {
     if (out_bf16)
-        launch(dequant_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(n), dim3(kThreads), 0, stream, codes,
-               scales, n, static_cast<uint16_t*>(out));
-    else
-        launch(dequant_kernel<float>, lane_grid<lane_width<float>()>(n), dim3(kThreads), 0, stream, codes,
-               scales, n, static_cast<float*>(out));
-    return hipGetLastError();
+        return launch(dequant_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(n), dim3(kThreads), 0, stream,
+                      codes, scales, n, static_cast<uint16_t*>(out));
+    return launch(dequant_kernel<float>, lane_grid<lane_width<float>()>(n), dim3(kThreads), 0, stream, codes,
+                  scales, n, static_cast<float*>(out));
 }
 
 // ---------------------------------------------------------------------------
@@ -310,20 +310,18 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
     const dim3 grid_f32 = lane_grid<lane_width<float>()>(C, fused_slices(nranks));
     const dim3 grid_bf16 = lane_grid<lane_width<uint16_t>()>(C, fused_slices(nranks));
     switch (nranks) {
-#define LPC_FUSED_CASE(NR)                                                                           \
-    case NR:                                                                                         \
-        if (out_bf16)                                                                                \
-            launch((rs_ag_fused_kernel<NR, uint16_t>), grid_bf16, block, 0, stream, in, peers, rank, \
-                   C, cc, cs, static_cast<uint16_t*>(out));                                          \
-        else                                                                                         \
-            launch((rs_ag_fused_kernel<NR, float>), grid_f32, block, 0, stream, in, peers, rank, C,  \
-                   cc, cs, static_cast<float*>(out));                                                \
-        break;
+#define LPC_FUSED_CASE(NR)                                                                                      \
+    case NR:                                                                                                    \
+        if (out_bf16)                                                                                           \
+            return launch(rs_ag_fused_kernel<NR, uint16_t>, grid_bf16, block, 0, stream, in, peers, rank, C, cc, \
+                          cs, static_cast<uint16_t*>(out));                                                     \
+        return launch(rs_ag_fused_kernel<NR, float>, grid_f32, block, 0, stream, in, peers, rank, C, cc, cs,     \
+                      static_cast<float*>(out));
         LPC_FUSED_CASE(1) LPC_FUSED_CASE(2) LPC_FUSED_CASE(3) LPC_FUSED_CASE(4)
         LPC_FUSED_CASE(5) LPC_FUSED_CASE(6) LPC_FUSED_CASE(7) LPC_FUSED_CASE(8)
 #undef LPC_FUSED_CASE
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -371,15 +369,13 @@ hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, h
     const dim3 grid((unsigned)((lanes + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
     uint16_t* o = static_cast<uint16_t*>(out);
     switch (nranks) {
-#define LPC_DDA_CASE(NR)                                                                 \
-    case NR:                                                                             \
-        launch((dda_flat_kernel<NR>), grid, block, 0, stream, b, n, o);      \
-        break;
+#define LPC_DDA_CASE(NR) \
+    case NR: return launch(dda_flat_kernel<NR>, grid, block, 0, stream, b, n, o);
         LPC_DDA_CASE(1) LPC_DDA_CASE(2) LPC_DDA_CASE(3) LPC_DDA_CASE(4)
         LPC_DDA_CASE(5) LPC_DDA_CASE(6) LPC_DDA_CASE(7) LPC_DDA_CASE(8)
 #undef LPC_DDA_CASE
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -440,16 +436,13 @@ hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank,
     switch (nranks) {
 #define LPC_TREE_CASE(NR)                                                                              \
     case NR:                                                                                           \
-        if (bf16)                                                                                      \
-            launch((dda_tree_rs_kernel<NR, true>), grid, block, 0, stream, b, off, ngran, out); \
-        else                                                                                           \
-            launch((dda_tree_rs_kernel<NR, false>), grid, block, 0, stream, b, off, ngran, out); \
-        break;
+        if (bf16) return launch(dda_tree_rs_kernel<NR, true>, grid, block, 0, stream, b, off, ngran, out); \
+        return launch(dda_tree_rs_kernel<NR, false>, grid, block, 0, stream, b, off, ngran, out);
         LPC_TREE_CASE(1) LPC_TREE_CASE(2) LPC_TREE_CASE(3) LPC_TREE_CASE(4)
         LPC_TREE_CASE(5) LPC_TREE_CASE(6) LPC_TREE_CASE(7) LPC_TREE_CASE(8)
 #undef LPC_TREE_CASE
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 __global__ __launch_bounds__(kThreads) void gather_copy_kernel(RankBufs chunks, size_t ngran,
@@ -465,9 +458,8 @@ hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size
                               hipStream_t stream) {
     const size_t esz = bf16 ? 2 : 4;
     const size_t ngran = n / nranks * esz / 16;
-    launch(gather_copy_kernel, grid_for(ngran, nranks), dim3(kThreads), 0, stream, chunks,
-                       ngran, static_cast<uint4*>(out));
-    return hipGetLastError();
+    return launch(gather_copy_kernel, grid_for(ngran, nranks), dim3(kThreads), 0, stream, chunks, ngran,
+                  static_cast<uint4*>(out));
 }
 
 // ---------------------------------------------------------------------------
@@ -757,9 +749,8 @@ hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32
                              int32_t* perm, hipStream_t stream) {
     size_t groups, tile;
     route_tiles(rows, &groups, &tile);
-    launch(a2av_route_kernel, dim3((unsigned)groups), dim3(kRouteThreads), 0, stream, dest, rows, nranks, tile,
-           counts, offsets, perm);
-    return hipGetLastError();
+    return launch(a2av_route_kernel, dim3((unsigned)groups), dim3(kRouteThreads), 0, stream, dest, rows, nranks,
+                  tile, counts, offsets, perm);
 }
 
 // ---------------------------------------------------------------------------
@@ -798,12 +789,10 @@ hipError_t launch_quantize_rows(const void* x, int in_bf16, size_t rows, size_t 
                                 uint8_t* codes, float* scales, hipStream_t stream) {
     const dim3 grid = grid_for(rows * row_len / kGranule), block(kThreads);
     if (in_bf16)
-        launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x), rows,
-               row_len, perm, codes, scales);
-    else
-        launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows, row_len,
-               perm, codes, scales);
-    return hipGetLastError();
+        return launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x), rows,
+                      row_len, perm, codes, scales);
+    return launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows, row_len,
+                  perm, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -826,8 +815,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 
 hipError_t launch_encode(const float* x, size_t n, uint8_t* codes, hipStream_t stream) {
     const size_t ngran = (n + 3) / 4;
-    launch(encode_kernel, grid_for(ngran), dim3(kThreads), 0, stream, x, n, codes);
-    return hipGetLastError();
+    return launch(encode_kernel, grid_for(ngran), dim3(kThreads), 0, stream, x, n, codes);
 }
 
 }  // namespace lpc

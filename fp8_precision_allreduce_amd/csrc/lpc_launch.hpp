@@ -1,7 +1,7 @@
 // lpc_launch.hpp -- launchers between the C ABI layer (lpc_api.hip) and the
 // kernels (lpc_kernels.hip).  Internal to liblpc.so.  Each launcher enqueues
-// one kernel on `stream` and returns hipGetLastError(); arguments have
-// already been validated by the caller.
+// one kernel on `stream` and returns the status of that launch; arguments
+// have already been validated by the caller.
 #pragma once
 
 #include <hip/hip_runtime.h>
