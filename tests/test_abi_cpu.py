@@ -248,3 +248,15 @@ def test_low_precision_switch_from_env(monkeypatch):
     assert comm.low_precision_from_env() is False
     c = comm.EmulatedComm(4, "cpu", low_precision=None)
     assert c.low_precision is False and c.get_size() == 4
+
+
+def test_launch_failure_is_reported(L):
+    """A call that passes validation reaches the launch; with no GPU visible the
+    launch itself fails, and that failure comes back as LPC_ERR_HIP (the status
+    of the launch, not of some earlier call)."""
+    assert L.lpc_quantize_fp8(A, F32, 128, A, A, None) == HIP
+    assert L.lpc_dequantize_fp8(A, A, 128, A, BF16, None) == HIP
+    assert L.dda_flat_reduce(arr(A, A), 2, 16, A, None) == HIP
+    assert L.lpc_a2av_route(A, 16, 8, A, A, A, None) == HIP
+    # validation still wins over the launch
+    assert L.lpc_quantize_fp8(A, F32, 100, A, A, None) == SHAPE
