@@ -218,16 +218,18 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, v
 
 // ---------------------------------------------------------------------------
 // (2)+(3) fused.  Every lane owns the same position i of every chunk.  The
-// peers' chunks are split into slices of two (peer q = rank + 1 .. rank + N - 1,
-// mod N): grid.y == 0 reduces and requantizes the own chunk at i, writes its
-// dequantization from registers, and dequantizes peers q = 1, 2 at i;
-// grid.y == y > 0 dequantizes peers q = 2y + 1, 2y + 2.  Each lane issues all
-// of its loads before its first conversion.  With bf16 output (W = 8) the
-// code loads are non-temporal: 15 streams are read once each, and keeping
-// them out of the caches measured faster at large sizes.
+// peers' chunks (peer q = rank + 1 .. rank + N - 1, mod N) are split into
+// slices of P = kPeersPerSlice: grid.y == 0 reduces and requantizes the own
+// chunk at i, writes its dequantization from registers, and dequantizes peers
+// q = 1 .. P at i; grid.y == y > 0 dequantizes peers q = P*y + 1 .. P*y + P.
+// One peer per slice measured fastest: 2, 3 or 7 per slice, or a slice 0 that
+// takes no peer, were 1-10% slower at 16 MiB fp32 and 256 MiB bf16.  Each lane
+// issues all of its loads before its first conversion.  With bf16 output
+// (W = 8) the code loads are non-temporal: 15 streams are read once each, and
+// keeping them out of the caches measured faster at large sizes.
 // ---------------------------------------------------------------------------
 
-constexpr int kPeersPerSlice = 2;
+constexpr int kPeersPerSlice = 1;
 
 __host__ __device__ constexpr int fused_slices(int N) {
     return N <= 1 ? 1 : (N - 1 + kPeersPerSlice - 1) / kPeersPerSlice;
