@@ -320,6 +320,35 @@ def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "chunk_blocks=%d" % chunk_blocks)
 
 
+def test_quantize_and_dequantize_at_the_largest_size(dev, orc):
+    """n = LPC_MAX_ELEMS (2^32 fp32 elements, 16 GiB): quantize and dequantize at
+    the largest accepted size, where byte offsets pass 2^32 and the grid is at its
+    widest.  Checked on blocks on both sides of every 1 GiB of input (so of every
+    4 GiB byte boundary), the first and last block, and 64 random blocks."""
+    n = lpc.MAX_ELEMS
+    nblk = n // BLOCK
+    say("quantize + dequantize at n = %d" % n)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(113)
+    x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32)
+    codes, scales = gpu_quantize(x)
+    back = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    lpc.lpc_dequantize_fp8(codes, scales, back)
+    torch.cuda.synchronize()
+    marks = [0, nblk - 1] + [k * (nblk // 16) + d for k in range(1, 16) for d in (-1, 0)]
+    rng = np.random.Generator(np.random.PCG64(113))
+    blocks = np.unique(np.concatenate([np.array(marks), rng.integers(0, nblk, 64)]))
+    bidx = torch.from_numpy(blocks).to(dev)
+    idx = (bidx[:, None] * BLOCK + torch.arange(BLOCK, device=dev)[None, :]).reshape(-1)
+    xb = to_host(x[idx])
+    rc, rs = orc.quantize(xb)
+    assert_same(to_host(codes[idx]), rc, "max-size codes")
+    assert_same(to_host(scales[bidx]), rs, "max-size scales")
+    assert_same(to_host(back[idx]), orc.dequantize(rc, rs, bf16=True), "max-size dequantize")
+    del x, codes, scales, back
+    torch.cuda.empty_cache()
+
+
 def test_graph_replays_match_eager(dev):
     """The benchmark times HIP graph replays: capture quantize + fused RS+AG + DDA
     flat, replay it three times with eager work and synchronisation in between,
@@ -365,6 +394,46 @@ def test_graph_replays_match_eager(dev):
         g.replay()
         torch.cuda.synchronize()
         for a, b in zip((q0c, q0s, own_c, own_s, out, dout), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep
+
+
+def test_graph_replays_match_eager_a2av(dev):
+    """All-to-all-v route + row quantize + dequantize captured in one HIP graph:
+    every replay reproduces the eager result (the router's multi-workgroup
+    counting keeps no state between calls)."""
+    rows, row_len = 5000, 1024
+    x = to_dev(inputs.a2av_rows(rows, row_len), dev)
+    dest = to_dev(inputs.zipf_destinations(rows=rows), dev)
+    counts = torch.empty(8, dtype=torch.int32, device=dev)
+    offsets = torch.empty(8, dtype=torch.int32, device=dev)
+    perm = torch.empty(rows, dtype=torch.int32, device=dev)
+    codes = torch.empty(rows * row_len, dtype=torch.uint8, device=dev)
+    scales = torch.empty(rows * row_len // BLOCK, dtype=torch.float32, device=dev)
+    back = torch.empty(rows, row_len, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        lpc.lpc_a2av_route(dest, 8, counts, offsets, perm)
+        lpc.lpc_quantize_fp8_rows(x, perm, codes, scales)
+        lpc.lpc_dequantize_fp8(codes, scales, back)
+
+    say("graph replay vs eager, all-to-all-v")
+    outs = (counts, offsets, perm, codes, scales, back)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep
 
 
