@@ -349,6 +349,57 @@ def test_quantize_and_dequantize_at_the_largest_size(dev, orc):
     torch.cuda.empty_cache()
 
 
+def test_fused_at_the_largest_size(dev, orc):
+    """The fused RS+AG at n = LPC_MAX_ELEMS per rank with N = 8 (the last rank, so
+    that the own chunk ends at element 2^32): every rank's quantized buffer, the
+    reduce-scatter chunks and the fp32 output, checked on sampled blocks of every
+    chunk, including each chunk's first and last block."""
+    N = 8
+    n = lpc.MAX_ELEMS
+    C = n // N
+    r = N - 1
+    say("fused RS+AG at n = %d, N = %d, rank %d" % (n, N, r))
+    gen = torch.Generator(device=dev)
+    rng = np.random.Generator(np.random.PCG64(127))
+    per_chunk = [np.unique(np.concatenate([[0, C // BLOCK - 1], rng.integers(0, C // BLOCK, 24)]))
+                 for _ in range(N)]
+    codes, scales, xb = [], [], []
+    for s_ in range(N):
+        gen.manual_seed(1000 + s_)
+        x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32)
+        c, sc = gpu_quantize(x)
+        codes.append(c)
+        scales.append(sc)
+        # inputs of the sampled blocks of every chunk, kept on the host
+        xb.append([to_host(x[(torch.from_numpy(p * C // BLOCK + per_chunk[p]).to(dev)[:, None] * BLOCK +
+                               torch.arange(BLOCK, device=dev)[None, :]).reshape(-1)]) for p in range(N)])
+        del x
+    cc = [torch.empty(C, dtype=torch.uint8, device=dev) for _ in range(N)]
+    cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    for p in range(N):
+        if p != r:
+            lpc.lpc_reduce_scatter_chunk(codes, scales, p, cc[p], cs[p])
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    lpc.lpc_rs_ag_fused(codes, scales, r, cc[r], cs[r], [None if p == r else cc[p] for p in range(N)],
+                        [None if p == r else cs[p] for p in range(N)], out)
+    torch.cuda.synchronize()
+    for p in range(N):
+        blocks = per_chunk[p]
+        qb = [orc.quantize(xb[s_][p]) for s_ in range(N)]
+        gidx = torch.from_numpy(((p * C // BLOCK + blocks)[:, None] * BLOCK + np.arange(BLOCK)[None, :])
+                                .reshape(-1)).to(dev)
+        for s_ in range(N):
+            assert_same(to_host(codes[s_][gidx]), qb[s_][0], "max-size codes rank %d chunk %d" % (s_, p))
+        sum_codes, sum_scales = orc.reduce_scatter_chunk([np.tile(c, N) for c, _ in qb],
+                                                         [np.tile(sc, N) for _, sc in qb], 0)
+        lidx = torch.from_numpy((blocks[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)).to(dev)
+        assert_same(to_host(cc[p][lidx]), sum_codes, "max-size chunk codes %d" % p)
+        assert_same(to_host(cs[p][torch.from_numpy(blocks).to(dev)]), sum_scales, "max-size chunk scales %d" % p)
+        assert_same(to_host(out[gidx]), orc.dequantize(sum_codes, sum_scales), "max-size out chunk %d" % p)
+    del codes, scales, cc, cs, out
+    torch.cuda.empty_cache()
+
+
 def test_graph_replays_match_eager(dev):
     """The benchmark times HIP graph replays: capture quantize + fused RS+AG + DDA
     flat, replay it three times with eager work and synchronisation in between,
