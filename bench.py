@@ -450,7 +450,7 @@ def main():
                 t.copy_(xs[0])
         ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, n, dt), dtype=torch.uint8, device=dev)
         r = stats(timer.run(lambda i: lpc.lpc_allreduce_emulated(ar_bufs[i % len(ar_bufs)], algo, ws), 8), 8)
-        r["what"] = "all 8 ranks' shares, one after another, in place"
+        r["what"] = "all 8 ranks' shares in place, one launch per step"
         kernels["allreduce_emulated_%s_n8_16MiB" % name] = r
         del ar_bufs, ws
     del tree_sets, tree_chunks, tree_out

@@ -2,14 +2,16 @@
 // size-based algorithm choice (the extern "C" calls of include/lpc.h's
 // "Allreduce over emulated ranks" section).
 //
-// Nothing here computes: an emulated allreduce enqueues, rank after rank, the
-// same per-rank entry points a real rank would call, with the other ranks'
-// buffers standing in for its peers' memory.  All arguments are checked
-// before the first call, so a validation error enqueues nothing.
+// An emulated allreduce runs each step of the algorithm for all ranks at
+// once: one launch per step, the rank taken from a grid dimension, each rank's
+// share computed exactly as the per-rank entry point computes it, with the
+// other ranks' buffers standing in for its peers' memory.  All arguments are
+// checked before the first launch, so a validation error enqueues nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "lpc.h"
+#include "lpc_launch.hpp"
 
 namespace {
 
@@ -78,6 +80,11 @@ size_t workspace_bytes(lpc_algo algo, int nranks, size_t n, lpc_dtype t) {
         if (st_ != LPC_OK) return st_;       \
     } while (0)
 
+#define LPC_TRY_HIP(expr)                              \
+    do {                                               \
+        if ((expr) != hipSuccess) return LPC_ERR_HIP;  \
+    } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -113,48 +120,52 @@ lpc_status lpc_allreduce_emulated(void* const bufs[], int nranks, size_t n, lpc_
     if (ws_bytes < workspace_bytes(algo, nranks, n, t)) return LPC_ERR_SHAPE;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const void* in[LPC_MAX_RANKS];
-    for (int r = 0; r < nranks; ++r) in[r] = bufs[r];
+    lpc::RankBufs in{};
+    for (int r = 0; r < nranks; ++r) in.p[r] = bufs[r];
 
     if (algo == LPC_ALGO_DDA_FLAT) {
-        // every rank reduces all buffers into its own output, then takes it in place
+        // every rank reduces all buffers into its own workspace output, then
+        // takes it in place
         const size_t slot = align_up(n * 2);
-        for (int r = 0; r < nranks; ++r) LPC_TRY(dda_flat_reduce(in, nranks, n, ws + r * slot, stream));
+        lpc::RankOut outs{};
+        for (int r = 0; r < nranks; ++r) outs.p[r] = ws + r * slot;
+        LPC_TRY_HIP(lpc::launch_dda_flat_ranks(in, nranks, n, outs, stream));
         for (int r = 0; r < nranks; ++r)
-            if (hipMemcpyAsync(bufs[r], ws + r * slot, n * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
-                return LPC_ERR_HIP;
+            LPC_TRY_HIP(hipMemcpyAsync(bufs[r], ws + r * slot, n * 2, hipMemcpyDeviceToDevice, stream));
         return LPC_OK;
     }
     if (algo == LPC_ALGO_DDA_TREE) {
         const size_t slot = align_up(n / (size_t)nranks * elem_bytes(t));
-        const void* chunks[LPC_MAX_RANKS];
+        lpc::RankOut chunks_out{}, outs{};
+        lpc::RankBufs chunks{};
         for (int r = 0; r < nranks; ++r) {
-            chunks[r] = ws + r * slot;
-            LPC_TRY(dda_tree_reduce_scatter(in, t, nranks, r, n, ws + r * slot, stream));
+            chunks_out.p[r] = ws + r * slot;
+            chunks.p[r] = ws + r * slot;
+            outs.p[r] = bufs[r];
         }
-        for (int r = 0; r < nranks; ++r) LPC_TRY(dda_tree_allgather(chunks, t, nranks, n, bufs[r], stream));
+        LPC_TRY_HIP(lpc::launch_dda_tree_rs_ranks(in, t == LPC_BF16, nranks, n, chunks_out, stream));
+        LPC_TRY_HIP(lpc::launch_dda_tree_ag_ranks(chunks, t == LPC_BF16, nranks, n, outs, stream));
         return LPC_OK;
     }
     // low precision: quantize every rank, reduce-scatter every chunk, all-gather into every buffer
     const LpLayout L = lp_layout(nranks, n);
-    const uint8_t* codes[LPC_MAX_RANKS];
-    const float* scales[LPC_MAX_RANKS];
-    const uint8_t* ccodes[LPC_MAX_RANKS];
-    const float* cscales[LPC_MAX_RANKS];
+    lpc::RankQuant q{}, cq{};
+    lpc::RankCodes codes{}, chunks{};
+    lpc::RankOut outs{};
     for (int r = 0; r < nranks; ++r) {
-        codes[r] = ws + L.codes[r];
-        scales[r] = reinterpret_cast<const float*>(ws + L.scales[r]);
-        ccodes[r] = ws + L.ccodes[r];
-        cscales[r] = reinterpret_cast<const float*>(ws + L.cscales[r]);
+        q.codes[r] = ws + L.codes[r];
+        q.scales[r] = reinterpret_cast<float*>(ws + L.scales[r]);
+        cq.codes[r] = ws + L.ccodes[r];
+        cq.scales[r] = reinterpret_cast<float*>(ws + L.cscales[r]);
+        codes.codes[r] = q.codes[r];
+        codes.scales[r] = q.scales[r];
+        chunks.codes[r] = cq.codes[r];
+        chunks.scales[r] = cq.scales[r];
+        outs.p[r] = bufs[r];
     }
-    for (int r = 0; r < nranks; ++r)
-        LPC_TRY(lpc_quantize_fp8(bufs[r], t, n, ws + L.codes[r], reinterpret_cast<float*>(ws + L.scales[r]),
-                                 stream));
-    for (int r = 0; r < nranks; ++r)
-        LPC_TRY(lpc_reduce_scatter_chunk(codes, scales, nranks, r, n, ws + L.ccodes[r],
-                                         reinterpret_cast<float*>(ws + L.cscales[r]), stream));
-    for (int r = 0; r < nranks; ++r)
-        LPC_TRY(lpc_allgather_dequant(ccodes, cscales, nranks, n, bufs[r], t, stream));
+    LPC_TRY_HIP(lpc::launch_quantize_ranks(in, t == LPC_BF16, nranks, n, q, stream));
+    LPC_TRY_HIP(lpc::launch_reduce_scatter_ranks(codes, nranks, n, cq, stream));
+    LPC_TRY_HIP(lpc::launch_allgather_ranks(chunks, nranks, n, outs, t == LPC_BF16, stream));
     return LPC_OK;
 }
 

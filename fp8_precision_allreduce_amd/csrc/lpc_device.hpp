@@ -51,6 +51,16 @@ struct RankBufs {
     const void* p[kMaxRanks];
 };
 
+// per-rank outputs of the all-ranks launches of the emulated collectives
+struct RankQuant {
+    uint8_t* codes[kMaxRanks];
+    float* scales[kMaxRanks];
+};
+
+struct RankOut {
+    void* p[kMaxRanks];
+};
+
 // ---------------------------------------------------------------------------
 // cross-lane block max (DPP inside 16-lane rows, ds_swizzle across rows)
 // ---------------------------------------------------------------------------

@@ -46,12 +46,10 @@ static hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t s
 // (1) quantize
 // ---------------------------------------------------------------------------
 
+// quantize granule g of x: codes non-temporal, the block's scale from its first lane
 template <typename In>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict__ x, size_t ngran,
-                                                            uint8_t* __restrict__ codes,
-                                                            float* __restrict__ scales) {
-    const size_t g = xcd_tile() * kThreads + threadIdx.x;
-    if (g >= ngran) return;  // whole 8-lane groups drop out together (n % 128 == 0)
+__device__ __forceinline__ void quantize_at(const In* __restrict__ x, size_t g, uint8_t* __restrict__ codes,
+                                            float* __restrict__ scales) {
     float v[kGranule];
     load16(x + g * kGranule, v);
     float s;
@@ -59,6 +57,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict
     const u32x4_t cv = {c.x, c.y, c.z, c.w};
     __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + g * kGranule));
     if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict__ x, size_t ngran,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+    const size_t g = xcd_tile() * kThreads + threadIdx.x;
+    if (g >= ngran) return;  // whole 8-lane groups drop out together (n % 128 == 0)
+    quantize_at(x, g, codes, scales);
 }
 
 hipError_t launch_quantize(const void* x, int in_bf16, size_t n, uint8_t* codes, float* scales,
@@ -336,11 +343,9 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
 constexpr int kDdaThreads = 64;
 constexpr int kDdaElems = 4;
 
+// this lane's elements e .. e+3 (fewer at the tail) of the flat reduce
 template <int N>
-__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t n,
-                                                               uint16_t* __restrict__ out) {
-    const size_t e = ((size_t)blockIdx.x * kDdaThreads + threadIdx.x) * kDdaElems;
-    if (e >= n) return;
+__device__ __forceinline__ void dda_flat_at(const RankBufs& b, size_t n, size_t e, uint16_t* __restrict__ out) {
     if (e + kDdaElems <= n) {
         uint2 v[N];
 #pragma unroll
@@ -366,6 +371,14 @@ __global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_
     }
 }
 
+template <int N>
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t n,
+                                                               uint16_t* __restrict__ out) {
+    const size_t e = ((size_t)blockIdx.x * kDdaThreads + threadIdx.x) * kDdaElems;
+    if (e >= n) return;
+    dda_flat_at<N>(b, n, e, out);
+}
+
 hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, hipStream_t stream) {
     const size_t lanes = (n + kDdaElems - 1) / kDdaElems;
     const dim3 grid((unsigned)((lanes + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
@@ -385,15 +398,13 @@ hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, h
 // Granule = 16 bytes (4 fp32 or 8 bf16).
 // ---------------------------------------------------------------------------
 
+// the rank-order sum of the 16-byte granule at byte offset `off` of every
+// rank's buffer, written to dst
 template <int N, bool BF16>
-__global__ __launch_bounds__(kThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes,
-                                                               size_t ngran, void* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= ngran) return;
+__device__ __forceinline__ void dda_tree_rs_at(const RankBufs& b, size_t off, void* __restrict__ dst) {
     uint4 v[N];
 #pragma unroll
-    for (int p = 0; p < N; ++p)
-        v[p] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(b.p[p]) + chunk_off_bytes + g * 16);
+    for (int p = 0; p < N; ++p) v[p] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(b.p[p]) + off);
     if (BF16) {
         float acc[8];
         const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
@@ -411,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void dda_tree_rs_kernel(RankBufs b, size_
                 acc[2 * k + 1] = acc[2 * k + 1] + bf16hi(w[k]);
             }
         }
-        reinterpret_cast<uint4*>(out)[g] =
+        *reinterpret_cast<uint4*>(dst) =
             make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
                        pack_bf16x2(acc[6], acc[7]));
     } else {
@@ -424,8 +435,16 @@ __global__ __launch_bounds__(kThreads) void dda_tree_rs_kernel(RankBufs b, size_
             acc.z = acc.z + d.z;
             acc.w = acc.w + d.w;
         }
-        reinterpret_cast<float4*>(out)[g] = acc;
+        *reinterpret_cast<float4*>(dst) = acc;
     }
+}
+
+template <int N, bool BF16>
+__global__ __launch_bounds__(kThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes,
+                                                               size_t ngran, void* __restrict__ out) {
+    const size_t g = granule_id();
+    if (g >= ngran) return;
+    dda_tree_rs_at<N, BF16>(b, chunk_off_bytes + g * 16, static_cast<uint4*>(out) + g);
 }
 
 hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank, size_t n, void* out,
@@ -818,6 +837,154 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 hipError_t launch_encode(const float* x, size_t n, uint8_t* codes, hipStream_t stream) {
     const size_t ngran = (n + 3) / 4;
     return launch(encode_kernel, grid_for(ngran), dim3(kThreads), 0, stream, x, n, codes);
+}
+
+// ---------------------------------------------------------------------------
+// All ranks in one launch (the emulated collectives on one GPU).  Each kernel
+// below runs the per-rank kernel of the same step for every rank at once,
+// with the rank taken from a grid dimension: every lane does exactly the
+// arithmetic of the per-rank kernel on the same elements, so the results are
+// those of N separate launches, bit for bit, at a third of the launches.
+// ---------------------------------------------------------------------------
+
+// quantize every rank's buffer: grid.y = rank
+template <typename In>
+__global__ __launch_bounds__(kThreads) void quantize_ranks_kernel(RankBufs x, size_t ngran, RankQuant q) {
+    const size_t g = xcd_tile() * kThreads + threadIdx.x;
+    if (g >= ngran) return;
+    const int r = blockIdx.y;
+    quantize_at(static_cast<const In*>(x.p[r]), g, q.codes[r], q.scales[r]);
+}
+
+hipError_t launch_quantize_ranks(const RankBufs& x, int in_bf16, int nranks, size_t n, const RankQuant& q,
+                                 hipStream_t stream) {
+    const size_t ngran = n / kGranule;
+    if (in_bf16)
+        return launch(quantize_ranks_kernel<uint16_t>, grid_for(ngran, nranks), dim3(kThreads), 0, stream, x,
+                      ngran, q);
+    return launch(quantize_ranks_kernel<float>, grid_for(ngran, nranks), dim3(kThreads), 0, stream, x, ngran, q);
+}
+
+// reduce-scatter step of every rank: grid.y = the rank owning the chunk
+template <int N>
+__global__ __launch_bounds__(kThreads) void reduce_scatter_ranks_kernel(RankCodes in, size_t C, RankQuant chunks) {
+    constexpr int W = rs_width<kRequant>();
+    const size_t i = lane_elem<W>();
+    if (i >= C) return;
+    const int r = blockIdx.y;
+    float acc[W];
+    rank_sum<N, W>(in, (size_t)r * C + i, acc);
+    float s;
+    const auto c = quantize_lane(acc, &s);
+    store_codes<W>(chunks.codes[r] + i, c);
+    if ((threadIdx.x & (kBlock / W - 1)) == 0) chunks.scales[r][i / kBlock] = s;
+}
+
+hipError_t launch_reduce_scatter_ranks(const RankCodes& in, int nranks, size_t n, const RankQuant& chunks,
+                                       hipStream_t stream) {
+    const size_t C = n / nranks;
+    const dim3 grid = lane_grid<rs_width<kRequant>()>(C, nranks), block(kThreads);
+    switch (nranks) {
+#define LPC_RSR_CASE(NR) \
+    case NR: return launch(reduce_scatter_ranks_kernel<NR>, grid, block, 0, stream, in, C, chunks);
+        LPC_RSR_CASE(1) LPC_RSR_CASE(2) LPC_RSR_CASE(3) LPC_RSR_CASE(4)
+        LPC_RSR_CASE(5) LPC_RSR_CASE(6) LPC_RSR_CASE(7) LPC_RSR_CASE(8)
+#undef LPC_RSR_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+// all-gather dequantization into every rank's output: grid.y = chunk, grid.z = rank
+template <typename Out>
+__global__ __launch_bounds__(kThreads) void allgather_ranks_kernel(RankCodes chunks, size_t C, RankOut outs) {
+    constexpr int W = lane_width<Out>();
+    const size_t i = lane_elem<W>();
+    if (i >= C) return;
+    const int p = blockIdx.y, r = blockIdx.z;
+    float d[W];
+    dequant_lane(load_codes<W, false>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
+    store_lane_nt(static_cast<Out*>(outs.p[r]) + (size_t)p * C + i, d);
+}
+
+hipError_t launch_allgather_ranks(const RankCodes& chunks, int nranks, size_t n, const RankOut& outs, int out_bf16,
+                                  hipStream_t stream) {
+    const size_t C = n / nranks;
+    if (out_bf16) {
+        dim3 grid = lane_grid<lane_width<uint16_t>()>(C, nranks);
+        grid.z = nranks;
+        return launch(allgather_ranks_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, chunks, C, outs);
+    }
+    dim3 grid = lane_grid<lane_width<float>()>(C, nranks);
+    grid.z = nranks;
+    return launch(allgather_ranks_kernel<float>, grid, dim3(kThreads), 0, stream, chunks, C, outs);
+}
+
+// DDA flat reduce of every rank into its own output: grid.y = rank
+template <int N>
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_ranks_kernel(RankBufs b, size_t n, RankOut outs) {
+    const size_t e = ((size_t)blockIdx.x * kDdaThreads + threadIdx.x) * kDdaElems;
+    if (e >= n) return;
+    dda_flat_at<N>(b, n, e, static_cast<uint16_t*>(outs.p[blockIdx.y]));
+}
+
+hipError_t launch_dda_flat_ranks(const RankBufs& b, int nranks, size_t n, const RankOut& outs, hipStream_t stream) {
+    const size_t lanes = (n + kDdaElems - 1) / kDdaElems;
+    const dim3 grid((unsigned)((lanes + kDdaThreads - 1) / kDdaThreads), nranks), block(kDdaThreads);
+    switch (nranks) {
+#define LPC_DDAR_CASE(NR) \
+    case NR: return launch(dda_flat_ranks_kernel<NR>, grid, block, 0, stream, b, n, outs);
+        LPC_DDAR_CASE(1) LPC_DDAR_CASE(2) LPC_DDAR_CASE(3) LPC_DDAR_CASE(4)
+        LPC_DDAR_CASE(5) LPC_DDAR_CASE(6) LPC_DDAR_CASE(7) LPC_DDAR_CASE(8)
+#undef LPC_DDAR_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+// DDA tree reduce-scatter of every rank: grid.y = the rank owning the chunk
+template <int N, bool BF16>
+__global__ __launch_bounds__(kThreads) void dda_tree_rs_ranks_kernel(RankBufs b, size_t chunk_bytes, size_t ngran,
+                                                                     RankOut chunks) {
+    const size_t g = granule_id();
+    if (g >= ngran) return;
+    const int r = blockIdx.y;
+    dda_tree_rs_at<N, BF16>(b, (size_t)r * chunk_bytes + g * 16, static_cast<uint4*>(chunks.p[r]) + g);
+}
+
+hipError_t launch_dda_tree_rs_ranks(const RankBufs& b, int bf16, int nranks, size_t n, const RankOut& chunks,
+                                    hipStream_t stream) {
+    const size_t chunk_bytes = n / nranks * (bf16 ? 2 : 4);
+    const size_t ngran = chunk_bytes / 16;
+    const dim3 grid = grid_for(ngran, nranks), block(kThreads);
+    switch (nranks) {
+#define LPC_TREER_CASE(NR)                                                                                   \
+    case NR:                                                                                                 \
+        if (bf16)                                                                                            \
+            return launch(dda_tree_rs_ranks_kernel<NR, true>, grid, block, 0, stream, b, chunk_bytes, ngran, \
+                          chunks);                                                                           \
+        return launch(dda_tree_rs_ranks_kernel<NR, false>, grid, block, 0, stream, b, chunk_bytes, ngran, chunks);
+        LPC_TREER_CASE(1) LPC_TREER_CASE(2) LPC_TREER_CASE(3) LPC_TREER_CASE(4)
+        LPC_TREER_CASE(5) LPC_TREER_CASE(6) LPC_TREER_CASE(7) LPC_TREER_CASE(8)
+#undef LPC_TREER_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+// DDA tree all-gather (a gather copy) into every rank's output: grid.y =
+// chunk, grid.z = rank
+__global__ __launch_bounds__(kThreads) void gather_copy_ranks_kernel(RankBufs chunks, size_t ngran, RankOut outs) {
+    const size_t g = granule_id();
+    if (g >= ngran) return;
+    const int p = blockIdx.y;
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(chunks.p[p])[g];
+    __builtin_nontemporal_store(v, static_cast<u32x4_t*>(outs.p[blockIdx.z]) + (size_t)p * ngran + g);
+}
+
+hipError_t launch_dda_tree_ag_ranks(const RankBufs& chunks, int bf16, int nranks, size_t n, const RankOut& outs,
+                                    hipStream_t stream) {
+    const size_t ngran = n / nranks * (bf16 ? 2 : 4) / 16;
+    dim3 grid = grid_for(ngran, nranks);
+    grid.z = nranks;
+    return launch(gather_copy_ranks_kernel, grid, dim3(kThreads), 0, stream, chunks, ngran, outs);
 }
 
 }  // namespace lpc

@@ -34,4 +34,17 @@ hipError_t launch_quantize_rows(const void* x, int in_bf16, size_t rows, size_t 
                                 uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_encode(const float* x, size_t n, uint8_t* codes, hipStream_t stream);
 
+// every rank's share of one step in a single launch (emulated collectives)
+hipError_t launch_quantize_ranks(const RankBufs& x, int in_bf16, int nranks, size_t n, const RankQuant& q,
+                                 hipStream_t stream);
+hipError_t launch_reduce_scatter_ranks(const RankCodes& in, int nranks, size_t n, const RankQuant& chunks,
+                                       hipStream_t stream);
+hipError_t launch_allgather_ranks(const RankCodes& chunks, int nranks, size_t n, const RankOut& outs, int out_bf16,
+                                  hipStream_t stream);
+hipError_t launch_dda_flat_ranks(const RankBufs& b, int nranks, size_t n, const RankOut& outs, hipStream_t stream);
+hipError_t launch_dda_tree_rs_ranks(const RankBufs& b, int bf16, int nranks, size_t n, const RankOut& chunks,
+                                    hipStream_t stream);
+hipError_t launch_dda_tree_ag_ranks(const RankBufs& chunks, int bf16, int nranks, size_t n, const RankOut& outs,
+                                    hipStream_t stream);
+
 }  // namespace lpc

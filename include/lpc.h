@@ -258,7 +258,8 @@ lpc_status lpc_allreduce_workspace_bytes(lpc_algo algo, int nranks, size_t n, lp
 /* In-place allreduce (SUM) over nranks emulated ranks on one GPU: every
  * bufs[r] ends with the elementwise sum over ranks, as the pages' Torchcomms
  * allreduce(t, SUM) leaves it on every rank.  Each rank's share runs as that
- * rank would run it, with the other ranks' buffers as its peers:
+ * rank would run it, with the other ranks' buffers as its peers; the ranks'
+ * shares of one step go in one launch (the rank is a grid dimension):
  *   DDA flat:      every rank's dda_flat_reduce into its workspace output,
  *                  then each output is copied into that rank's buffer;
  *   DDA tree:      every rank's dda_tree_reduce_scatter into the workspace,
@@ -272,7 +273,8 @@ lpc_status lpc_allreduce_workspace_bytes(lpc_algo algo, int nranks, size_t n, lp
  *              bf16 (LPC_ERR_DTYPE); shapes as the entry points it calls
  *   workspace  device, 16-byte aligned, at least the bytes
  *              lpc_allreduce_workspace_bytes gives (else LPC_ERR_SHAPE)
- * The work is enqueued on `stream`; nothing is enqueued on error.          */
+ * The work is enqueued on `stream`.  A validation error enqueues nothing; a
+ * refused launch (LPC_ERR_HIP) may leave the steps before it enqueued.     */
 lpc_status lpc_allreduce_emulated(void *const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
