@@ -31,8 +31,10 @@ cache-warm DDA figure is reported beside the cold one.
 value = algorithmic bytes of one fused RS+AG launch / its mean duration
 (GB/s).  roofline compares it with the 8 TB/s HBM peak; traffic is the HBM
 byte count per launch from rocprofv3 counters (profiles/traffic.json), null
-when those counters were taken on other kernel sources.  cpu_baseline is the
-CPU oracle on a bounded sample of the same share.
+when those counters were taken on other kernel sources.  For context the
+roofline object also carries the mean duration of an empty launch timed the
+same way (empty_launch_us) and the rate of the fused launch beyond it.
+cpu_baseline is the CPU oracle on a bounded sample of the same share.
 
 Extra per-kernel lines (not part of the step): the unfused reduce-scatter
 and all-gather, the one-quantization low-precision reduce-scatter, the DDA
@@ -401,6 +403,9 @@ def main():
         dda_res["%dKiB" % (m * 2 // 1024)] = r
     warm = stats(timer.run(lambda i: dda(4, i % 4), K), K)
     dda_res["64KiB"]["us_warm"] = warm["us"]
+    # the same batch of launches of a kernel that does nothing (one lane, no memory): the fixed cost
+    # every launch above pays before it moves a byte
+    floor_us = timer.run(lambda i: torch.cuda._sleep(0), L)[0]
 
     # -- the same two headline kernels as graph replays (back to back inside one graph) --------------------
     g_fused = GraphTimer(torch, fused, L)
@@ -566,6 +571,9 @@ def main():
             "bytes_per_launch": fb,
             "mean_us": round(f_us, 3),
             "launches": kernels["rs_ag_fused_f32_16MiB"]["launches"],
+            # context: an empty launch's share of mean_us on this machine, and the rate of the rest
+            "empty_launch_us": round(floor_us, 3),
+            "beyond_empty_launch_gbps": round(fb / max(f_us - floor_us, 1e-3) / 1e3, 1),
         },
         "kernels": kernels,
         "dda_flat_n8_bf16": dda_res,
