@@ -304,6 +304,37 @@ def test_lp_allreduce_rank_counts(dev, orc, N, bf16, fused):
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "N=%d" % N)
 
 
+def _random_case(g):
+    """Rank count, size, dtype and a mix of block magnitudes drawn from g: blocks
+    scaled by 10^U(-30, 30), zero blocks, blocks with a single huge outlier."""
+    N = int(g.integers(1, 9))
+    blocks = int(g.integers(1, 48))
+    n = BLOCK * N * blocks
+    bf16 = bool(g.integers(0, 2))
+    xs = []
+    for _ in range(N):
+        x = g.standard_normal(n).astype(np.float32).reshape(-1, BLOCK)
+        x *= (10.0 ** g.uniform(-30, 30, (x.shape[0], 1))).astype(np.float32)
+        x[g.random(x.shape[0]) < 0.05] = 0.0
+        hot = g.random(x.shape[0]) < 0.05
+        x[hot, g.integers(0, BLOCK)] *= np.float32(1e4)
+        x = np.nan_to_num(x.reshape(-1), posinf=np.float32(3e38), neginf=np.float32(-3e38))
+        xs.append(inputs.truncate_to_bf16(x) if bf16 else x)
+    return N, n, bf16, xs
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_lp_allreduce_random_cases(dev, orc, seed):
+    """Randomly drawn rank counts, sizes, dtypes and block magnitudes (seeded), both
+    paths (fused on even seeds), every intermediate against the oracle."""
+    g = np.random.Generator(np.random.PCG64(900 + seed))
+    N, n, bf16, xs = _random_case(g)
+    fused = seed % 2 == 0
+    say("lp allreduce random seed=%d N=%d n=%d bf16=%s fused=%s" % (seed, N, n, bf16, fused))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.bfloat16 if bf16 else torch.float32, fused)
+    compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "random seed %d" % seed)
+
+
 @pytest.mark.parametrize("chunk_blocks", [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 63, 64, 65, 8 * 64 + 3])
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
