@@ -495,11 +495,11 @@ hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size
 // array itself: 4 bytes a row, re-read from L2, and a handful of VALU
 // operations per row, against a placement pass that would otherwise run on
 // one CU.  The number of workgroups is capped, which bounds the re-reading.
-//   counting  a lane loads 4 rows with one 16-byte load, 16 sub-tiles at a
-//             time; a row adds one to its destination's byte of a 64-bit
+//   counting  a lane loads 4 rows with one 16-byte load, 8 or 16 sub-tiles
+//             at a time; a row adds one to its destination's byte of a 64-bit
 //             per-lane counter, folded into 32-bit counters before a byte can
 //             overflow; then a workgroup-wide sum.
-//   placing   1024 rows at a time, 4 contiguous rows per lane: each lane
+//   placing   one sub-tile (4 contiguous rows per lane) at a time: each lane
 //             counts its rows per destination in eight 16-bit fields, an
 //             exclusive scan over the lanes gives each row the number of
 //             earlier rows of its destination in the sub-tile, and the
@@ -511,12 +511,24 @@ hipError_t launch_dda_tree_ag(const RankBufs& chunks, int bf16, int nranks, size
 // part of perm past the last placed row with -1.
 // ---------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteRowsPerLane = 4;
-constexpr size_t kRouteSubTile = (size_t)kRouteThreads * kRouteRowsPerLane;  // 1024 rows
-constexpr int kRouteUnroll = 16;            // sub-tiles in flight per lane while counting
 constexpr size_t kRouteMaxGroups = 128;
+
+// Workgroup size and counting depth.  256 lanes with 16 sub-tiles in flight
+// measured fastest up to about 18K rows (5.5 us at 16,384); 512 lanes with 8
+// from there on (64K rows 10.6 -> 8.8 us, 256K rows 31.1 -> 21.3 us): the
+// counting, which every workgroup repeats over all rows, then runs on twice
+// the wavefronts of a CU.
+template <int THREADS, int UNROLL>
+struct RouteCfg {
+    static constexpr int kThreads = THREADS;
+    static constexpr int kWaves = THREADS / 64;
+    static constexpr int kUnroll = UNROLL;                                 // sub-tiles in flight while counting
+    static constexpr size_t kSubTile = (size_t)THREADS * kRouteRowsPerLane;  // rows placed per step
+};
+using RouteSmall = RouteCfg<256, 16>;
+using RouteLarge = RouteCfg<512, 8>;
+constexpr size_t kRouteLargeFrom = 18432;  // rows
 
 // Sum over the wavefront, in every lane: DPP inside each 16-lane row (xor 1,
 // xor 2, half-row mirror, row mirror), then the four row sums via readlane.
@@ -567,34 +579,56 @@ __device__ __forceinline__ uint64_t dest_byte(int32_t d, int nranks) {
     return (uint64_t)((uint32_t)d < (uint32_t)nranks ? 1u : 0u) << ((d & 7) * 8);
 }
 
-// This lane's per-destination counts of the rows before row `split` and of
-// the rest (split % 1024 == 0).  The lane reads rows 4*t + 1024*u, 16
-// sub-tiles per round with all 16 loads in flight (rows past the end read as
-// -1); a sub-tile lies wholly on one side of `split`.
-__device__ __forceinline__ void count_rows(const int32_t* __restrict__ dest, size_t rows, int nranks,
-                                           size_t split, uint32_t (&before)[kMaxRanks],
-                                           uint32_t (&after)[kMaxRanks]) {
-    for (size_t s0 = 0; s0 < rows; s0 += kRouteUnroll * kRouteSubTile) {
-        int4 v[kRouteUnroll];
+// One round of count_rows: kUnroll sub-tiles from row s0, all loads in
+// flight.  A full round (every row in range) loads plainly; the last, partial
+// round loads only the sub-tiles that hold rows (a uniform test), each through
+// load_raw4 (rows past the end read as -1).
+template <typename Cfg, bool kFull>
+__device__ __forceinline__ void count_round(const int32_t* __restrict__ dest, size_t rows, int nranks,
+                                            size_t split, size_t s0, uint32_t (&before)[kMaxRanks],
+                                            uint32_t (&after)[kMaxRanks]) {
+    const size_t lane = (size_t)kRouteRowsPerLane * threadIdx.x;
+    int4 v[Cfg::kUnroll];
 #pragma unroll
-        for (int u = 0; u < kRouteUnroll; ++u)
-            v[u] = load_raw4(dest, rows, s0 + u * kRouteSubTile + (size_t)kRouteRowsPerLane * threadIdx.x);
-        uint64_t lo = 0, hi = 0;  // at most 64 per byte
+    for (int u = 0; u < Cfg::kUnroll; ++u) {
+        const size_t s = s0 + u * Cfg::kSubTile;
+        if (kFull)
+            v[u] = *reinterpret_cast<const int4*>(dest + s + lane);
+        else if (s < rows)
+            v[u] = load_raw4(dest, rows, s + lane);
+    }
+    uint64_t lo = 0, hi = 0;  // at most 64 per byte
 #pragma unroll
-        for (int u = 0; u < kRouteUnroll; ++u) {
+    for (int u = 0; u < Cfg::kUnroll; ++u) {
+        const size_t s = s0 + u * Cfg::kSubTile;
+        if (kFull || s < rows) {
             const uint64_t b = dest_byte(v[u].x, nranks) + dest_byte(v[u].y, nranks) + dest_byte(v[u].z, nranks) +
                                dest_byte(v[u].w, nranks);
-            if (s0 + u * kRouteSubTile < split)
+            if (s < split)
                 lo += b;
             else
                 hi += b;
         }
-#pragma unroll
-        for (int j = 0; j < kMaxRanks; ++j) {
-            before[j] += (uint32_t)(lo >> (8 * j)) & 0xFFu;
-            after[j] += (uint32_t)(hi >> (8 * j)) & 0xFFu;
-        }
     }
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+        before[j] += (uint32_t)(lo >> (8 * j)) & 0xFFu;
+        after[j] += (uint32_t)(hi >> (8 * j)) & 0xFFu;
+    }
+}
+
+// This lane's per-destination counts of the rows before row `split` and of
+// the rest (split a multiple of the sub-tile).  The lane reads rows
+// 4*t + kSubTile*u of each round; a sub-tile lies wholly on one side of
+// `split`.
+template <typename Cfg>
+__device__ __forceinline__ void count_rows(const int32_t* __restrict__ dest, size_t rows, int nranks,
+                                           size_t split, uint32_t (&before)[kMaxRanks],
+                                           uint32_t (&after)[kMaxRanks]) {
+    constexpr size_t kRound = Cfg::kUnroll * Cfg::kSubTile;
+    size_t s0 = 0;
+    for (; s0 + kRound <= rows; s0 += kRound) count_round<Cfg, true>(dest, rows, nranks, split, s0, before, after);
+    if (s0 < rows) count_round<Cfg, false>(dest, rows, nranks, split, s0, before, after);
 }
 
 // 16-bit field d & 7 of four packed registers (destinations 2r, 2r+1 in
@@ -647,13 +681,14 @@ __device__ __forceinline__ void place_rows(const int32_t (&d)[kRouteRowsPerLane]
         if ((uint32_t)d[i] < (uint32_t)nranks) perm[pos[i]] = (int32_t)(k + i);
 }
 
-__global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t* __restrict__ dest,
+template <typename Cfg>
+__global__ __launch_bounds__(Cfg::kThreads) void a2av_route_kernel(const int32_t* __restrict__ dest,
                                                                    size_t rows, int nranks, size_t tile,
                                                                    int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ perm) {
-    __shared__ uint32_t wave_part[kRouteWaves][2 * kMaxRanks];
-    __shared__ uint32_t wave_tot[kRouteWaves][4];
+    __shared__ uint32_t wave_part[Cfg::kWaves][2 * kMaxRanks];
+    __shared__ uint32_t wave_tot[Cfg::kWaves][4];
     const int t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wavefront index, kept scalar
     const size_t ts = (size_t)blockIdx.x * tile;
@@ -666,7 +701,7 @@ __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t
     uint32_t before[kMaxRanks], after[kMaxRanks];
 #pragma unroll
     for (int j = 0; j < kMaxRanks; ++j) before[j] = after[j] = 0;
-    count_rows(dest, rows, nranks, ts, before, after);
+    count_rows<Cfg>(dest, rows, nranks, ts, before, after);
 
     int32_t d[kRouteRowsPerLane] = {first.x, first.y, first.z, first.w};
     uint32_t own[4], excl[4];
@@ -694,7 +729,7 @@ __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t
     for (int j = 0; j < kMaxRanks; ++j) {
         bef[j] = tot[j] = 0;
 #pragma unroll
-        for (int v = 0; v < kRouteWaves; ++v) {
+        for (int v = 0; v < Cfg::kWaves; ++v) {
             bef[j] += wave_part[v][j];
             tot[j] += wave_part[v][kMaxRanks + j];
         }
@@ -723,14 +758,14 @@ __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t
         for (int r = 0; r < 4; ++r) {
             sub[r] = 0;
 #pragma unroll
-            for (int v = 0; v < kRouteWaves; ++v) {
+            for (int v = 0; v < Cfg::kWaves; ++v) {
                 const uint32_t c = wave_tot[v][r];
                 excl[r] += v < w ? c : 0u;
                 sub[r] += c;
             }
         }
         place_rows(d, nranks, k, excl, base, perm);
-        s += kRouteSubTile;
+        s += Cfg::kSubTile;
         if (s >= te) break;
 #pragma unroll
         for (int j = 0; j < kMaxRanks; ++j) base[j] += field16(sub, j);
@@ -754,24 +789,26 @@ __global__ __launch_bounds__(kRouteThreads) void a2av_route_kernel(const int32_t
 
     // the tail of perm past the placed rows
     const size_t q0 = placed > ts ? placed : ts;
-    for (size_t q = q0 + t; q < te; q += kRouteThreads) perm[q] = -1;
+    for (size_t q = q0 + t; q < te; q += Cfg::kThreads) perm[q] = -1;
 }
 
-// Workgroups and tile size: one 1024-row sub-tile per workgroup up to
-// kRouteMaxGroups workgroups, larger tiles (whole sub-tiles) beyond.
-static void route_tiles(size_t rows, size_t* groups, size_t* tile) {
-    const size_t subtiles = (rows + kRouteSubTile - 1) / kRouteSubTile;
+// Workgroups and tile size: one sub-tile per workgroup up to kRouteMaxGroups
+// workgroups, larger tiles (whole sub-tiles) beyond.
+template <typename Cfg>
+static hipError_t launch_route(const int32_t* dest, size_t rows, int nranks, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, hipStream_t stream) {
+    const size_t subtiles = (rows + Cfg::kSubTile - 1) / Cfg::kSubTile;
     const size_t g = subtiles < kRouteMaxGroups ? subtiles : kRouteMaxGroups;
-    *tile = (subtiles + g - 1) / g * kRouteSubTile;
-    *groups = (rows + *tile - 1) / *tile;
+    const size_t tile = (subtiles + g - 1) / g * Cfg::kSubTile;
+    const size_t groups = (rows + tile - 1) / tile;
+    return launch(a2av_route_kernel<Cfg>, dim3((unsigned)groups), dim3(Cfg::kThreads), 0, stream, dest, rows, nranks,
+                  tile, counts, offsets, perm);
 }
 
 hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32_t* counts, int32_t* offsets,
                              int32_t* perm, hipStream_t stream) {
-    size_t groups, tile;
-    route_tiles(rows, &groups, &tile);
-    return launch(a2av_route_kernel, dim3((unsigned)groups), dim3(kRouteThreads), 0, stream, dest, rows, nranks,
-                  tile, counts, offsets, perm);
+    if (rows < kRouteLargeFrom) return launch_route<RouteSmall>(dest, rows, nranks, counts, offsets, perm, stream);
+    return launch_route<RouteLarge>(dest, rows, nranks, counts, offsets, perm, stream);
 }
 
 // ---------------------------------------------------------------------------
