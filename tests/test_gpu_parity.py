@@ -656,10 +656,13 @@ def test_dda_tree(dev, orc, bf16):
 # -- all-to-all-v ----------------------------------------------------------------------------------
 
 def test_a2av_route_cfg5(dev, orc):
-    # one workgroup per 1024-row sub-tile up to 128 workgroups, then larger
-    # tiles: sizes around a sub-tile, ragged tails and multi-sub-tile tiles
+    # one workgroup per sub-tile (1024 rows, 2048 from 18,432 rows) up to 128
+    # workgroups, then larger tiles: sizes around a sub-tile, ragged tails,
+    # multi-sub-tile tiles, whole counting rounds (16 x 1024 and 8 x 2048
+    # rows) with and without a partial round, and both sides of the switch
     for rows, nranks in ((inputs.A2AV_ROWS, 8), (1, 8), (1000, 3), (1023, 8), (1024, 8), (1025, 5),
-                         (4097, 1), (70_000, 8), (140_000, 7), (300_001, 8)):
+                         (4097, 1), (16_383, 8), (16_384, 6), (16_385, 8), (18_431, 8), (18_432, 8),
+                         (32_768, 4), (34_817, 8), (70_000, 8), (140_000, 7), (300_001, 8)):
         dest = inputs.zipf_destinations(rows=rows, nranks=nranks)
         say("a2av route rows=%d nranks=%d" % (rows, nranks))
         counts = torch.empty(nranks, dtype=torch.int32, device=dev)
