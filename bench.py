@@ -40,8 +40,9 @@ cpu_baseline is the CPU oracle on a bounded sample of the same share.
 Extra per-kernel lines (not part of the step): the unfused reduce-scatter
 and all-gather, the one-quantization low-precision reduce-scatter, the DDA
 tree phases at 2 MiB bf16 per rank, the full emulated 8-rank allreduce
-(low precision and DDA tree), the N=8 x 256 MiB bf16 fused launch, and the
-all-to-all-v route, row quantize and dequantize at 16,384 x 7168 bf16.
+(low precision and DDA tree), the N=8 x 256 MiB bf16 fused launch, the fp32
+fused launch at 16, 32, 64 and 128 MiB per rank, and the all-to-all-v route,
+row quantize and dequantize at 16,384 x 7168 bf16.
 """
 from __future__ import annotations
 
@@ -282,7 +283,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the per-kernel lines outside the step (256 MiB bf16, all-to-all-v)")
+                    help="skip the per-kernel lines outside the step (256 MiB bf16, fused by size, all-to-all-v)")
     ap.add_argument("--dda-sets", type=int, default=0,
                     help="DDA buffer sets cycled through (0: enough to exceed the 256 MB cache)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -564,6 +565,60 @@ def main():
         del sets4, b4, a4
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+
+        # The fused kernel against message size: fp32, N=8, values as in the 16 MiB workload.  The
+        # launch's fixed cost weighs less as the message grows.  Copies are cycled so that together
+        # they hold at least three times the Infinity Cache.
+        sizes = {}
+        for mib in (16, 32, 64, 128):
+            ns = mib * 2 ** 20 // 4
+            Cs = ns // N
+            layout = [ns, ns // BLOCK * 4] * N + [Cs, Cs // BLOCK * 4] * (N + 1) + [ns * 4]
+            copies = max(2, -(-3 * MALL_BYTES // sum(layout)))
+            sets_s = []
+            for k in range(copies):
+                a_s = Arena(torch, dev, layout)
+                b_s = dict(codes=[], scales=[], cc=[], cs=[])
+                for r in range(N):
+                    b_s["codes"].append(a_s.take(ns, torch.uint8))
+                    b_s["scales"].append(a_s.take(ns // BLOCK, torch.float32))
+                for r in range(N):
+                    b_s["cc"].append(a_s.take(Cs, torch.uint8))
+                    b_s["cs"].append(a_s.take(Cs // BLOCK, torch.float32))
+                b_s["oc"], b_s["os"] = a_s.take(Cs, torch.uint8), a_s.take(Cs // BLOCK, torch.float32)
+                b_s["out"] = a_s.take(ns, torch.float32)
+                if k == 0:
+                    for r in range(N):
+                        xs_r = inputs.device_rank_buffer(3, r, dev, n=ns)
+                        lpc.lpc_quantize_fp8(xs_r, b_s["codes"][r], b_s["scales"][r])
+                        del xs_r
+                    for r in range(N):
+                        lpc.lpc_reduce_scatter_chunk(b_s["codes"], b_s["scales"], r, b_s["cc"][r], b_s["cs"][r])
+                else:
+                    for key in ("codes", "scales", "cc", "cs"):
+                        for dst, src in zip(b_s[key], sets_s[0][key]):
+                            dst.copy_(src)
+                sets_s.append(b_s)
+            torch.cuda.synchronize()
+
+            def fused_s(i, sets_s=sets_s):
+                b = sets_s[i % len(sets_s)]
+                lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["oc"], b["os"], [None] + b["cc"][1:],
+                                    [None] + b["cs"][1:], b["out"])
+
+            for i in range(2 * copies):
+                fused_s(i)
+            torch.cuda.synchronize()
+            d = stats(timer.run(fused_s, 40), 40, fused_bytes(ns, N, 4))
+            d["frac"] = round(d["gbps"] / HBM_PEAK_GBPS, 4)
+            d["copies"] = copies
+            sizes["%dMiB" % mib] = d
+            for b in sets_s:
+                assert torch.equal(b["oc"], sets_s[0]["cc"][0]), "fused %d MiB: reduced chunk differs" % mib
+            del sets_s, b_s, a_s, fused_s
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        kernels["rs_ag_fused_f32_by_size"] = sizes
 
         rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
         m5 = rows * row_len
