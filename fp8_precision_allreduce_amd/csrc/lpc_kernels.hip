@@ -515,8 +515,8 @@ constexpr int kRouteRowsPerLane = 4;
 constexpr size_t kRouteMaxGroups = 128;
 
 // Workgroup size and counting depth.  256 lanes with 16 sub-tiles in flight
-// measured fastest up to about 18K rows (5.5 us at 16,384); 512 lanes with 8
-// from there on (64K rows 10.6 -> 8.8 us, 256K rows 31.1 -> 21.3 us): the
+// measured fastest up to about 18K rows (4.5 us at 16,384); 512 lanes with 8
+// from there on (64K rows 9.2 -> 7.8 us, 256K rows 28.3 -> 20.2 us): the
 // counting, which every workgroup repeats over all rows, then runs on twice
 // the wavefronts of a CU.
 template <int THREADS, int UNROLL>
@@ -530,33 +530,56 @@ using RouteSmall = RouteCfg<256, 16>;
 using RouteLarge = RouteCfg<512, 8>;
 constexpr size_t kRouteLargeFrom = 18432;  // rows
 
-// Sum over the wavefront, in every lane: DPP inside each 16-lane row (xor 1,
-// xor 2, half-row mirror, row mirror), then the four row sums via readlane.
-// Needs all 64 lanes active.
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-    int x = (int)v;
-    x += __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);
-    return (uint32_t)(__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
-                      __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+// Wavefront totals of 16 per-lane counters, transposed: lane l ends with the
+// total of counter l & 15.  Four DPP steps (row mirror, half-row mirror,
+// quad xor 2, quad xor 1) each pair a lane with one that holds the same
+// counters; the lane keeps the half selected by one bit of its row position
+// (a bit the two partners differ in) and adds the partner's copy of that half.
+// After them each lane of a row holds one counter summed over the row, and two
+// gfx950 lane swaps add lane l ^ 32, then lane l ^ 16.  About 50 VALU
+// operations, against 16 separate reductions.  Needs all 64 lanes active.
+__device__ __forceinline__ uint32_t wave_sums16(const uint32_t (&c)[16]) {
+    const unsigned l = threadIdx.x & 15;
+    uint32_t a[8], b[4], d[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bool hi = (l & 8) != 0;
+        const int send = (int)(hi ? c[j] : c[j + 8]);
+        a[j] = (hi ? c[j + 8] : c[j]) + (uint32_t)__builtin_amdgcn_update_dpp(0, send, 0x140, 0xF, 0xF, false);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool hi = (l & 4) != 0;
+        const int send = (int)(hi ? a[j] : a[j + 4]);
+        b[j] = (hi ? a[j + 4] : a[j]) + (uint32_t)__builtin_amdgcn_update_dpp(0, send, 0x141, 0xF, 0xF, false);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const bool hi = (l & 2) != 0;
+        const int send = (int)(hi ? b[j] : b[j + 2]);
+        d[j] = (hi ? b[j + 2] : b[j]) + (uint32_t)__builtin_amdgcn_update_dpp(0, send, 0x4E, 0xF, 0xF, false);
+    }
+    const bool hi = (l & 1) != 0;
+    const int send = (int)(hi ? d[0] : d[1]);
+    uint32_t v = (hi ? d[1] : d[0]) + (uint32_t)__builtin_amdgcn_update_dpp(0, send, 0xB1, 0xF, 0xF, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // lanes l and l ^ 32
+    v = h[0] + h[1];
+    const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // lanes l and l ^ 16
+    return q[0] + q[1];
 }
 
 // Inclusive prefix sum over the lanes of the wavefront: row_shr 1, 2, 4, 8
 // inside each 16-lane row (a lane with no source lane in its row adds 0), then
-// the totals of the rows below, via readlane.  Needs all 64 lanes active.
+// row_bcast 15 (rows 1 and 3 add the last lane of the row below) and row_bcast
+// 31 (rows 2 and 3 add lane 31).  Needs all 64 lanes active.
 __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     int x = (int)v;
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
     x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
     x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
     x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
-    const int r0 = __builtin_amdgcn_readlane(x, 15);
-    const int r1 = __builtin_amdgcn_readlane(x, 31);
-    const int r2 = __builtin_amdgcn_readlane(x, 47);
-    const int row = (threadIdx.x & 63) >> 4;
-    x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
     return (uint32_t)x;
 }
 
@@ -579,10 +602,23 @@ __device__ __forceinline__ uint64_t dest_byte(int32_t d, int nranks) {
     return (uint64_t)((uint32_t)d < (uint32_t)nranks ? 1u : 0u) << ((d & 7) * 8);
 }
 
+// The count bytes of four rows.  When all four name a destination in 0..7
+// (the usual case) each adds one at byte d with no test against nranks: a row
+// naming a destination in nranks..7 then lands in a byte that the kernel
+// clears after the reduction.  Otherwise every row is tested (dest_byte).
+// This saves about two VALU operations a row.
+__device__ __forceinline__ uint64_t row_bytes4(int4 v, int nranks) {
+    if ((uint32_t)(v.x | v.y | v.z | v.w) < 8u)
+        return (1ull << ((uint32_t)v.x << 3)) + (1ull << ((uint32_t)v.y << 3)) + (1ull << ((uint32_t)v.z << 3)) +
+               (1ull << ((uint32_t)v.w << 3));
+    return dest_byte(v.x, nranks) + dest_byte(v.y, nranks) + dest_byte(v.z, nranks) + dest_byte(v.w, nranks);
+}
+
 // One round of count_rows: kUnroll sub-tiles from row s0, all loads in
-// flight.  A full round (every row in range) loads plainly; the last, partial
-// round loads only the sub-tiles that hold rows (a uniform test), each through
-// load_raw4 (rows past the end read as -1).
+// flight.  A full round (every row in range) loads plainly and counts through
+// row_bytes4; the last, partial round loads only the sub-tiles that hold rows
+// (a uniform test), each through load_raw4 (rows past the end read as -1), and
+// tests every row.
 template <typename Cfg, bool kFull>
 __device__ __forceinline__ void count_round(const int32_t* __restrict__ dest, size_t rows, int nranks,
                                             size_t split, size_t s0, uint32_t (&before)[kMaxRanks],
@@ -602,8 +638,9 @@ __device__ __forceinline__ void count_round(const int32_t* __restrict__ dest, si
     for (int u = 0; u < Cfg::kUnroll; ++u) {
         const size_t s = s0 + u * Cfg::kSubTile;
         if (kFull || s < rows) {
-            const uint64_t b = dest_byte(v[u].x, nranks) + dest_byte(v[u].y, nranks) + dest_byte(v[u].z, nranks) +
-                               dest_byte(v[u].w, nranks);
+            const uint64_t b = kFull ? row_bytes4(v[u], nranks)
+                                     : dest_byte(v[u].x, nranks) + dest_byte(v[u].y, nranks) +
+                                           dest_byte(v[u].z, nranks) + dest_byte(v[u].w, nranks);
             if (s < split)
                 lo += b;
             else
@@ -712,14 +749,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void a2av_route_kernel(const int32_t
         excl[r] = incl - own[r];
         if ((t & 63) == 63) wave_tot[w][r] = incl;
     }
+    static_assert(2 * kMaxRanks == 16, "one counter per lane of a row");
+    uint32_t cnt[2 * kMaxRanks];
 #pragma unroll
     for (int j = 0; j < kMaxRanks; ++j) {
-        const uint32_t b = wave_sum(before[j]), a = wave_sum(after[j]);
-        if ((t & 63) == 0) {
-            wave_part[w][j] = b;
-            wave_part[w][kMaxRanks + j] = a;
-        }
+        cnt[j] = before[j];
+        cnt[kMaxRanks + j] = after[j];
     }
+    const uint32_t wave_cnt = wave_sums16(cnt);
+    if ((t & 63) < 2 * kMaxRanks) wave_part[w][t & 63] = wave_cnt;
     __syncthreads();
 
     // every lane: totals, offsets and the bases of this tile's first
@@ -734,6 +772,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void a2av_route_kernel(const int32_t
             tot[j] += wave_part[v][kMaxRanks + j];
         }
         tot[j] += bef[j];
+        if (j >= nranks) bef[j] = tot[j] = 0;  // rows row_bytes4 counted for no destination
     }
     uint32_t base[kMaxRanks], off[kMaxRanks], placed = 0;
 #pragma unroll

@@ -661,7 +661,7 @@ def test_a2av_route_cfg5(dev, orc):
     # multi-sub-tile tiles, whole counting rounds (16 x 1024 and 8 x 2048
     # rows) with and without a partial round, and both sides of the switch
     for rows, nranks in ((inputs.A2AV_ROWS, 8), (1, 8), (1000, 3), (1023, 8), (1024, 8), (1025, 5),
-                         (4097, 1), (16_383, 8), (16_384, 6), (16_385, 8), (18_431, 8), (18_432, 8),
+                         (4097, 1), (16_383, 8), (16_384, 6), (16_385, 8), (17_408, 8), (18_431, 8), (18_432, 8),
                          (32_768, 4), (34_817, 8), (70_000, 8), (140_000, 7), (300_001, 8)):
         dest = inputs.zipf_destinations(rows=rows, nranks=nranks)
         say("a2av route rows=%d nranks=%d" % (rows, nranks))
@@ -691,17 +691,22 @@ def test_a2av_route_drops_bad_destinations_large(dev, orc):
     """Out-of-range destinations spread over many workgroups: the valid rows are
     routed as the oracle routes them alone, and perm's tail is -1."""
     rng = np.random.default_rng(11)
-    for rows, bad in ((5000, 0.15), (140_000, 0.02), (3000, 1.0)):
-        dest = inputs.zipf_destinations(rows=rows, nranks=8).copy()
+    # bad values: negative, at or past 8, and (with fewer than 8 ranks) in nranks..7,
+    # spread over whole counting rounds and partial ones
+    for rows, bad, nranks in ((5000, 0.15, 8), (140_000, 0.02, 8), (3000, 1.0, 8), (40_000, 0.05, 5),
+                              (20_000, 0.3, 3), (16_384, 0.1, 7), (70_001, 0.01, 2)):
+        dest = inputs.zipf_destinations(rows=rows, nranks=nranks).copy()
         hit = rng.random(rows) < bad
-        dest[hit] = np.where(rng.random(int(hit.sum())) < 0.5, -1, 8 + rng.integers(0, 5, int(hit.sum())))
-        say("a2av route rows=%d with %d out-of-range destinations" % (rows, int(hit.sum())))
-        counts = torch.empty(8, dtype=torch.int32, device=dev)
-        offsets = torch.empty(8, dtype=torch.int32, device=dev)
+        pool = np.array([-1, -7, 8, 9, 12, 2 ** 31 - 1] + list(range(nranks, 8)), np.int64)
+        dest[hit] = pool[rng.integers(0, pool.size, int(hit.sum()))].astype(np.int32)
+        say("a2av route rows=%d nranks=%d with %d out-of-range destinations" % (rows, nranks, int(hit.sum())))
+        counts = torch.empty(nranks, dtype=torch.int32, device=dev)
+        offsets = torch.empty(nranks, dtype=torch.int32, device=dev)
         perm = torch.empty(rows, dtype=torch.int32, device=dev)
-        lpc.lpc_a2av_route(to_dev(dest, dev), 8, counts, offsets, perm)
+        lpc.lpc_a2av_route(to_dev(dest, dev), nranks, counts, offsets, perm)
         keep = np.nonzero(~hit)[0].astype(np.int32)
-        rc, ro, rp = orc.a2av_route(dest[keep], 8) if keep.size else (np.zeros(8, np.int32),) * 2 + (keep,)
+        rc, ro, rp = (orc.a2av_route(dest[keep], nranks) if keep.size
+                      else (np.zeros(nranks, np.int32),) * 2 + (keep,))
         want = np.full(rows, -1, np.int32)
         want[:keep.size] = keep[rp]
         assert_same(to_host(counts), rc, "counts")
