@@ -788,15 +788,15 @@ def _oracle_allreduce(orc, xs, algo, bf16):
     return orc.lp_allreduce(xs, bf16=bf16)["out"]
 
 
-@pytest.mark.parametrize("algo", [lpc.ALGO_DDA_FLAT, lpc.ALGO_DDA_TREE, lpc.ALGO_LOW_PRECISION],
-                         ids=["dda_flat", "dda_tree", "low_precision"])
-@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("algo,bf16", [(lpc.ALGO_DDA_FLAT, True), (lpc.ALGO_DDA_TREE, False),
+                                       (lpc.ALGO_DDA_TREE, True), (lpc.ALGO_LOW_PRECISION, False),
+                                       (lpc.ALGO_LOW_PRECISION, True)],
+                         ids=["dda_flat-bf16", "dda_tree-f32", "dda_tree-bf16", "low_precision-f32",
+                              "low_precision-bf16"])
 @pytest.mark.parametrize("N", [2, 5, 8])
 def test_allreduce_emulated(dev, orc, algo, bf16, N):
     """Every rank's buffer after lpc_allreduce_emulated equals the oracle's result of
-    the same algorithm (DDA flat is bf16 only)."""
-    if algo == lpc.ALGO_DDA_FLAT and not bf16:
-        pytest.skip("DDA flat reduces bf16 only")
+    the same algorithm (DDA flat is bf16 only: see the next test)."""
     n = BLOCK * N * 23
     xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
     if bf16:
@@ -810,6 +810,23 @@ def test_allreduce_emulated(dev, orc, algo, bf16, N):
     ref = _oracle_allreduce(orc, xs, algo, bf16)
     for r in range(N):
         assert_same(to_host(bufs[r]), ref, "allreduce %s rank %d" % (lpc.ALGO_NAMES[algo], r))
+
+
+def test_allreduce_emulated_dda_flat_rejects_f32(dev):
+    """DDA flat reduces bf16 only: fp32 buffers are refused before anything is
+    enqueued, and the buffers are left as they were."""
+    N, n = 4, BLOCK * 4 * 3
+    bufs = [torch.full((n,), float(r + 1), dtype=torch.float32, device=dev) for r in range(N)]
+    with pytest.raises(lpc.LpcError) as e:
+        lpc.lpc_allreduce_workspace_bytes(lpc.ALGO_DDA_FLAT, N, n, torch.float32)
+    assert e.value.status_name == "LPC_ERR_DTYPE"
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    with pytest.raises(lpc.LpcError) as e:
+        lpc.lpc_allreduce_emulated(bufs, lpc.ALGO_DDA_FLAT, ws)
+    assert e.value.status_name == "LPC_ERR_DTYPE"
+    torch.cuda.synchronize()
+    for r in range(N):
+        assert torch.equal(bufs[r], torch.full((n,), float(r + 1), dtype=torch.float32, device=dev))
 
 
 def test_allreduce_emulated_full_size_lp(dev, orc):
