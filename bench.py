@@ -306,10 +306,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     N = NRANKS
-    n = inputs.CONFIGS[3]["n"]
+    n = inputs.WORKLOADS[inputs.LP_16MIB]["n"]
     C = n // N
     log("generating workload: N=%d x %d fp32 per rank" % (N, n))
-    xs_host = [inputs.rank_buffer(3, r) for r in range(N)]
+    xs_host = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(N)]
 
     # -- untimed setup: every rank's quantized buffer and reduced chunk ------------------
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
@@ -513,7 +513,7 @@ def main():
         # fused launch) already exceeds the 256 MB Infinity Cache, but a kernel relaunched on the
         # same buffers still finds part of them there (quantize bf16: 58 against 70 us).
         COPIES = 2
-        n4 = inputs.CONFIGS[4]["n"]
+        n4 = inputs.WORKLOADS[inputs.LP_256MIB_BF16]["n"]
         C4 = n4 // N
         sets4 = []
         for k in range(COPIES):
@@ -529,7 +529,7 @@ def main():
             b4["out"] = a4.take(n4, torch.bfloat16)
             if k == 0:
                 for r in range(N):
-                    x4 = inputs.device_rank_buffer(4, r, dev)
+                    x4 = inputs.device_rank_buffer(inputs.LP_256MIB_BF16, r, dev)
                     lpc.lpc_quantize_fp8(x4, b4["codes"][r], b4["scales"][r])
                     if r == 0:
                         b4["x"].copy_(x4)
@@ -589,7 +589,7 @@ def main():
                 b_s["out"] = a_s.take(ns, torch.float32)
                 if k == 0:
                     for r in range(N):
-                        xs_r = inputs.device_rank_buffer(3, r, dev, n=ns)
+                        xs_r = inputs.device_rank_buffer(inputs.LP_16MIB, r, dev, n=ns)
                         lpc.lpc_quantize_fp8(xs_r, b_s["codes"][r], b_s["scales"][r])
                         del xs_r
                     for r in range(N):

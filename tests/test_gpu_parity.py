@@ -188,11 +188,11 @@ def _edge_blocks():
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_quantize_matches_oracle(dev, orc, bf16):
     cases = {
-        "cfg1_rank0": inputs.rank_buffer(1, 0),
-        "ragged_37blocks": inputs.rank_buffer(1, 1, 37 * BLOCK),
-        "one_block": inputs.rank_buffer(1, 2, BLOCK),
+        "lp_n4_64k_rank0": inputs.rank_buffer(inputs.LP_SMALL, 0),
+        "ragged_37blocks": inputs.rank_buffer(inputs.LP_SMALL, 1, 37 * BLOCK),
+        "one_block": inputs.rank_buffer(inputs.LP_SMALL, 2, BLOCK),
         "edge_blocks": _edge_blocks(),
-        "cfg3_sample": inputs.rank_buffer(3, 0, 33 * 4096 + 5 * BLOCK),
+        "lp_n8_16MiB_sample": inputs.rank_buffer(inputs.LP_16MIB, 0, 33 * 4096 + 5 * BLOCK),
     }
     for name, x in cases.items():
         if bf16:
@@ -260,7 +260,7 @@ def test_quantize_near_midpoints(dev, orc):
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_dequantize_matches_oracle(dev, orc, bf16):
-    x = np.concatenate([inputs.rank_buffer(1, 3, 41 * BLOCK), _edge_blocks()])
+    x = np.concatenate([inputs.rank_buffer(inputs.LP_SMALL, 3, 41 * BLOCK), _edge_blocks()])
     c, s = orc.quantize(x)
     say("dequantize", x.size, "bf16" if bf16 else "f32")
     out = torch.empty(x.size, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
@@ -280,12 +280,12 @@ def test_zero_size_calls_are_noops(dev):
 # -- low-precision allreduce ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
-def test_lp_allreduce_cfg1(dev, orc, fused):
-    N = inputs.CONFIGS[1]["nranks"]
-    xs = [inputs.rank_buffer(1, r) for r in range(N)]
-    say("lp allreduce cfg1 N=%d n=%d fused=%s" % (N, xs[0].size, fused))
+def test_lp_allreduce_n4_64k(dev, orc, fused):
+    N = inputs.WORKLOADS[inputs.LP_SMALL]["nranks"]
+    xs = [inputs.rank_buffer(inputs.LP_SMALL, r) for r in range(N)]
+    say("lp allreduce N=%d n=%d fused=%s" % (N, xs[0].size, fused))
     res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, fused)
-    compare_allreduce(res, orc.lp_allreduce(xs), "cfg1")
+    compare_allreduce(res, orc.lp_allreduce(xs), "n4 64k")
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
@@ -296,7 +296,7 @@ def test_lp_allreduce_rank_counts(dev, orc, N, bf16, fused):
     number of blocks, so the last wavefront is half empty, and a workgroup count
     that is not a multiple of the 8 XCDs), both dtypes, fused and unfused."""
     n = BLOCK * N * 37
-    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r, n) for r in range(N)]
     if bf16:
         xs = [inputs.truncate_to_bf16(x) for x in xs]
     say("lp allreduce N=%d n=%d bf16=%s fused=%s" % (N, n, bf16, fused))
@@ -343,7 +343,7 @@ def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
     the XCD-aware order is visited exactly once, for both lane widths."""
     N = 8
     n = BLOCK * N * chunk_blocks
-    xs = [inputs.rank_buffer(1, r, n) for r in range(N)]
+    xs = [inputs.rank_buffer(inputs.LP_SMALL, r, n) for r in range(N)]
     if bf16:
         xs = [inputs.truncate_to_bf16(x) for x in xs]
     say("fused chunk of %d blocks, N=8, bf16=%s" % (chunk_blocks, bf16))
@@ -438,7 +438,7 @@ def test_graph_replays_match_eager(dev):
     N = 8
     n = BLOCK * N * 40
     C = n // N
-    xs = [to_dev(inputs.rank_buffer(3, r, n), dev) for r in range(N)]
+    xs = [to_dev(inputs.rank_buffer(inputs.LP_16MIB, r, n), dev) for r in range(N)]
     q = [gpu_quantize(x) for x in xs]
     codes = [c for c, _ in q]
     scales = [s for _, s in q]
@@ -534,24 +534,24 @@ def test_lp_allreduce_pages_example(dev):
             assert torch.all(out[:n] == N * (N - 1) / 2)
 
 
-def test_lp_allreduce_cfg3_full(dev, orc):
-    """Workload 3 at full size (N=8, 16 MiB fp32 per rank, outliers), every intermediate."""
+def test_lp_allreduce_n8_16MiB_full(dev, orc):
+    """The 16 MiB workload at full size (N=8, 16 MiB fp32 per rank, outliers), every intermediate."""
     N = 8
-    xs = [inputs.rank_buffer(3, r) for r in range(N)]
-    say("lp allreduce cfg3 full N=8 n=%d" % xs[0].size)
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(N)]
+    say("lp allreduce 16 MiB full N=8 n=%d" % xs[0].size)
     res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32)
-    compare_allreduce(res, orc.lp_allreduce(xs), "cfg3")
+    compare_allreduce(res, orc.lp_allreduce(xs), "n8 16MiB")
 
 
-def test_lp_allreduce_cfg4_sampled(dev, orc):
-    """Workload 4 at full size (N=8, 256 MiB bf16 per rank, Laplace): the whole path
+def test_lp_allreduce_n8_256MiB_bf16_sampled(dev, orc):
+    """The 256 MiB bf16 workload at full size (N=8, 256 MiB bf16 per rank, Laplace): the whole path
     on the GPU (fused kernel for ranks 0 and 7), checked on 96 sampled blocks per
     chunk: every rank's codes and scales there, the reduced chunk, and the output."""
     N = 8
-    n = inputs.CONFIGS[4]["n"]
+    n = inputs.WORKLOADS[inputs.LP_256MIB_BF16]["n"]
     C = n // N
-    say("lp allreduce cfg4 full-size N=8 n=%d (sampled check)" % n)
-    xs = [inputs.device_rank_buffer(4, r, dev) for r in range(N)]
+    say("lp allreduce 256 MiB bf16 full-size N=8 n=%d (sampled check)" % n)
+    xs = [inputs.device_rank_buffer(inputs.LP_256MIB_BF16, r, dev) for r in range(N)]
     q = [gpu_quantize(x) for x in xs]
     codes = [c for c, _ in q]
     scales = [s for _, s in q]
@@ -576,9 +576,9 @@ def test_lp_allreduce_cfg4_sampled(dev, orc):
             xb = [to_host(x[idx]) for x in xs]                   # inputs of those blocks, every rank
             for s_ in range(N):
                 rc, rs = orc.quantize(xb[s_], bf16=True)
-                assert_same(to_host(codes[s_][idx]), rc, "cfg4 codes rank %d" % s_)
+                assert_same(to_host(codes[s_][idx]), rc, "256 MiB codes rank %d" % s_)
                 assert_same(to_host(scales[s_][torch.from_numpy(p * C // BLOCK + blocks).to(dev)]), rs,
-                            "cfg4 scales rank %d" % s_)
+                            "256 MiB scales rank %d" % s_)
             # the sampled blocks form a little allreduce of their own (block-local arithmetic)
             qb = [orc.quantize(x, bf16=True) for x in xb]
             m = blocks.size * BLOCK
@@ -586,10 +586,10 @@ def test_lp_allreduce_cfg4_sampled(dev, orc):
                                                              [np.tile(s, N) for _, s in qb], 0)
             assert sum_codes.size == m
             lidx = torch.from_numpy((blocks[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)).to(dev)
-            assert_same(to_host(cc[p][lidx]), sum_codes, "cfg4 chunk codes %d" % p)
-            assert_same(to_host(cs[p][torch.from_numpy(blocks).to(dev)]), sum_scales, "cfg4 chunk scales %d" % p)
+            assert_same(to_host(cc[p][lidx]), sum_codes, "256 MiB chunk codes %d" % p)
+            assert_same(to_host(cs[p][torch.from_numpy(blocks).to(dev)]), sum_scales, "256 MiB chunk scales %d" % p)
             ref_out = orc.dequantize(sum_codes, sum_scales, bf16=True)
-            assert_same(to_host(out[idx]), ref_out, "cfg4 out rank %d chunk %d" % (r, p))
+            assert_same(to_host(out[idx]), ref_out, "256 MiB out rank %d chunk %d" % (r, p))
         del out
     del xs, codes, scales, cc, cs
     torch.cuda.empty_cache()
@@ -600,7 +600,7 @@ def test_lp_reduce_scatter_one_quantization(dev, orc, bf16):
     """Low-precision ReduceScatter: the FP32 rank-order sum of the owned chunk, unquantized."""
     N = 8
     n = BLOCK * N * 19
-    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r, n) for r in range(N)]
     q = [orc.quantize(x) for x in xs]
     codes = [to_dev(c, dev) for c, _ in q]
     scales = [to_dev(s, dev) for _, s in q]
@@ -615,7 +615,7 @@ def test_lp_reduce_scatter_one_quantization(dev, orc, bf16):
 # -- DDA ----------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("tokens", inputs.DDA_TOKENS)
-def test_dda_flat_cfg2(dev, orc, tokens):
+def test_dda_flat_message_sizes(dev, orc, tokens):
     bufs = inputs.dda_buffers(tokens)
     say("dda flat N=8 hidden 8192 x %d tokens" % tokens)
     out = torch.empty(bufs[0].size, dtype=torch.bfloat16, device=dev)
@@ -625,7 +625,7 @@ def test_dda_flat_cfg2(dev, orc, tokens):
 
 @pytest.mark.parametrize("N,n", [(1, 8), (2, 3), (3, 1001), (8, 8 * 977 + 5), (5, 4096 * 3 + 7)])
 def test_dda_flat_ragged(dev, orc, N, n):
-    bufs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(2, r), n, 0.5)) for r in range(N)]
+    bufs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5)) for r in range(N)]
     say("dda flat ragged N=%d n=%d" % (N, n))
     out = torch.empty(n, dtype=torch.bfloat16, device=dev)
     lpc.dda_flat_reduce([to_dev(b, dev) for b in bufs], out)
@@ -635,7 +635,7 @@ def test_dda_flat_ragged(dev, orc, N, n):
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_dda_tree(dev, orc, bf16):
     N, n = 8, 8 * 8 * 1001
-    fb = [inputs.normal_f32(inputs.rng(2, r), n, 0.5) for r in range(N)]
+    fb = [inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5) for r in range(N)]
     bufs = [inputs.truncate_to_bf16(x) for x in fb] if bf16 else fb
     dt = torch.bfloat16 if bf16 else torch.float32
     bd = [to_dev(b, dev) for b in bufs]
@@ -655,7 +655,7 @@ def test_dda_tree(dev, orc, bf16):
 
 # -- all-to-all-v ----------------------------------------------------------------------------------
 
-def test_a2av_route_cfg5(dev, orc):
+def test_a2av_route_sizes(dev, orc):
     # one workgroup per sub-tile (1024 rows, 2048 from 18,432 rows) up to 128
     # workgroups, then larger tiles: sizes around a sub-tile, ragged tails,
     # multi-sub-tile tiles, whole counting rounds (16 x 1024 and 8 x 2048
@@ -736,7 +736,7 @@ def test_a2av_quantize_rows_small(dev, orc):
         assert_same(to_host(codes), rc, "rows codes")
         assert_same(to_host(scales), rs, "rows scales")
     # rows longer than 1024 granules take the multi-workgroup path
-    x2 = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(5, 1), 6 * 128 * 130, 1.0)).reshape(6, -1)
+    x2 = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.A2AV, 1), 6 * 128 * 130, 1.0)).reshape(6, -1)
     p2 = np.array([5, 0, 3, 1, 4, 2], np.int32)
     say("a2av quantize long rows", x2.shape)
     codes = torch.empty(x2.shape, dtype=torch.uint8, device=dev)
@@ -747,11 +747,11 @@ def test_a2av_quantize_rows_small(dev, orc):
     assert_same(to_host(scales), rs, "long rows scales")
 
 
-def test_a2av_cfg5_full_sampled(dev, orc):
-    """Workload 5 at full size: route, quantize + pack all 16,384 x 7168 rows, dequantize
+def test_a2av_16384x7168_sampled(dev, orc):
+    """The all-to-all-v workload at full size: route, quantize + pack all 16,384 x 7168 rows, dequantize
     the packed buffer; 192 packed rows checked against the oracle."""
     rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
-    say("a2av cfg5 full rows=%d row_len=%d" % (rows, row_len))
+    say("a2av full rows=%d row_len=%d" % (rows, row_len))
     x = inputs.a2av_rows()
     dest = inputs.zipf_destinations()
     xd, dd = to_dev(x, dev), to_dev(dest, dev)
@@ -766,15 +766,15 @@ def test_a2av_cfg5_full_sampled(dev, orc):
     lpc.lpc_dequantize_fp8(codes, scales, back)
     torch.cuda.synchronize()
     rc, ro, rp = orc.a2av_route(dest, 8)
-    assert_same(to_host(perm), rp, "cfg5 perm")
+    assert_same(to_host(perm), rp, "a2av perm")
     assert int(to_host(counts).sum()) == rows
     g = np.random.Generator(np.random.PCG64(109))
     ks = np.concatenate([[0, rows - 1], ro, g.choice(rows, 180, replace=False)]).astype(np.int64)
     for k in ks:
         c, s = orc.quantize(x[rp[k]], bf16=True)
-        assert_same(to_host(codes[k]), c, "cfg5 packed row %d codes" % k)
-        assert_same(to_host(scales[k]), s, "cfg5 packed row %d scales" % k)
-        assert_same(to_host(back[k]), orc.dequantize(c, s, bf16=True), "cfg5 dequant row %d" % k)
+        assert_same(to_host(codes[k]), c, "a2av packed row %d codes" % k)
+        assert_same(to_host(scales[k]), s, "a2av packed row %d scales" % k)
+        assert_same(to_host(back[k]), orc.dequantize(c, s, bf16=True), "a2av dequant row %d" % k)
 
 
 # -- emulated allreduce (size-based dispatch, torchcomms-shaped wrapper) ------------------------------
@@ -798,7 +798,7 @@ def test_allreduce_emulated(dev, orc, algo, bf16, N):
     """Every rank's buffer after lpc_allreduce_emulated equals the oracle's result of
     the same algorithm (DDA flat is bf16 only: see the next test)."""
     n = BLOCK * N * 23
-    xs = [inputs.rank_buffer(3, r, n) for r in range(N)]
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r, n) for r in range(N)]
     if bf16:
         xs = [inputs.truncate_to_bf16(x) for x in xs]
     say("allreduce emulated algo=%s N=%d n=%d bf16=%s" % (lpc.ALGO_NAMES[algo], N, n, bf16))
@@ -830,10 +830,10 @@ def test_allreduce_emulated_dda_flat_rejects_f32(dev):
 
 
 def test_allreduce_emulated_full_size_lp(dev, orc):
-    """Workload 3 at full size through the emulated allreduce (low precision): every
+    """The 16 MiB workload at full size through the emulated allreduce (low precision): every
     rank's buffer equals the oracle's allreduce output."""
     N = 8
-    xs = [inputs.rank_buffer(3, r) for r in range(N)]
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(N)]
     say("allreduce emulated low precision, N=8 x 16 MiB")
     bufs = [to_dev(x, dev) for x in xs]
     algo = lpc.lpc_select_algo(N, xs[0].size, torch.float32, True)
@@ -876,7 +876,7 @@ def test_a2av_quantize_rows_more_than_grid_y(dev, orc):
     """70,000 short rows: more rows than one launch's grid.y (65,535), so workgroups loop
     over rows; perm from the router, checked in full against the oracle."""
     rows, row_len = 70_000, 128
-    x = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(5, 2), rows * row_len, 1.0)).reshape(rows, row_len)
+    x = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.A2AV, 2), rows * row_len, 1.0)).reshape(rows, row_len)
     dest = inputs.zipf_destinations(rows=rows)
     say("a2av quantize rows=%d row_len=%d" % (rows, row_len))
     counts = torch.empty(8, dtype=torch.int32, device=dev)
@@ -896,7 +896,7 @@ def test_a2av_quantize_rows_more_than_grid_y(dev, orc):
 def test_a2av_quantize_rows_f32(dev, orc):
     """Row gather + quantize from fp32 rows (3 blocks per row), with invalid perm entries."""
     rows, row_len = 257, 384
-    x = inputs.normal_f32(inputs.rng(5, 3), rows * row_len, 1.0).reshape(rows, row_len)
+    x = inputs.normal_f32(inputs.rng(inputs.A2AV, 3), rows * row_len, 1.0).reshape(rows, row_len)
     _, _, perm = orc.a2av_route(inputs.zipf_destinations(rows=rows), 8)
     p = perm.copy()
     p[3] = -7
