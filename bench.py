@@ -291,7 +291,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the N ranks are emulated as N buffers "
+        print("bench.py: this benchmark runs on one GPU only (the N ranks are emulated as N buffers "
               "in one GPU's HBM); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -696,7 +696,7 @@ def main():
             "bytes_per_launch": fb,
             "mean_us": round(f_us, 3),
             "launches": kernels["rs_ag_fused_f32_16MiB"]["launches"],
-            # context: an empty launch's share of mean_us on this machine, and the rate of the rest
+            # context: an empty launch's share of mean_us on this GPU, and the rate of the rest
             "empty_launch_us": round(floor_us, 3),
             "beyond_empty_launch_gbps": round(fb / max(f_us - floor_us, 1e-3) / 1e3, 1),
         },

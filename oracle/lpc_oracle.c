@@ -22,7 +22,7 @@
  *    section on Direct Data Access: DDA flat (every rank loads all peers'
  *    buffers and reduces locally) and DDA tree (reduce-scatter + all-gather).
  * The pages give no FP8 variant, block size, scale rule or summation order.
- * This oracle takes the readings fixed for the build: OCP FP8 E4M3FN,
+ * Where they are silent this oracle takes these readings: OCP FP8 E4M3FN,
  * round-to-nearest-even, saturating at +-448, one FP32 scale
  * s = absmax/448 per 128 contiguous elements, FP32 sums in rank order
  * 0..N-1, the owned chunk of rank r is elements [r*C, (r+1)*C), C = n/N.
