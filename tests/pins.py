@@ -309,6 +309,8 @@ def pin_rs_rank_order(o):
             acc = (acc + d[p][sl]).astype(np.float32)
         got = o.reduce_scatter_out(codes, scales, r)
         assert np.array_equal(bits(got), bits(acc))
+        # bf16 output: torch's round-to-nearest-even cast of that FP32 sum
+        assert np.array_equal(o.reduce_scatter_out(codes, scales, r, bf16=True), torch_bf16(acc))
         # the requantized chunk is the blockwise quantization of that same sum
         cc, cs = o.reduce_scatter_chunk(codes, scales, r)
         qc, qs = o.quantize(acc)
@@ -512,6 +514,12 @@ def pin_a2av_rows(o):
     c, s = o.quantize(x.reshape(-1), bf16=True)
     ci, si = o.quantize_rows(x, np.arange(rows, dtype=np.int32), bf16=True)
     assert np.array_equal(ci.reshape(-1), c) and np.array_equal(si.reshape(-1), s)
+    # fp32 rows: the same per source row
+    x32 = inputs.normal_f32(np.random.Generator(np.random.PCG64(53)), rows * row_len, 1.0).reshape(rows, row_len)
+    codes32, scales32 = o.quantize_rows(x32, perm, bf16=False)
+    for k in range(rows):
+        c, s = o.quantize(x32[perm[k]])
+        assert np.array_equal(codes32[k], c) and np.array_equal(bits(scales32[k]), bits(s))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

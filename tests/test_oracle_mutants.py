@@ -61,6 +61,13 @@ MUTANTS = {
     "route_inclusive_offsets": ("        offsets[d] = (int32_t)pos;\n        pos += (size_t)counts[d];",
                                 "        pos += (size_t)counts[d];\n        offsets[d] = (int32_t)pos;"),
     "rows_not_gathered": ("size_t src = (size_t)perm[k];", "size_t src = k;"),
+    "rows_f32_half_stride": ("lpo_quantize_f32((const float *)x + src * row_len, row_len,",
+                             "lpo_quantize_f32((const float *)x + src * (row_len / 2), row_len,"),
+    "rs_out_bf16_truncates": ("            ((uint16_t *)out)[i] = lpo_bf16_rne(acc);\n        else\n"
+                              "            ((float *)out)[i] = acc;",
+                              "            { uint32_t u_; memcpy(&u_, &acc, 4); ((uint16_t *)out)[i] = (uint16_t)(u_ >> 16); }\n"
+                              "        else\n"
+                              "            ((float *)out)[i] = acc;"),
 }
 
 
