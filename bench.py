@@ -39,10 +39,10 @@ cpu_baseline is the CPU oracle on a bounded sample of the same share.
 
 Extra per-kernel lines (not part of the step): the unfused reduce-scatter
 and all-gather, the one-quantization low-precision reduce-scatter, the DDA
-tree phases at 2 MiB bf16 per rank, the full emulated 8-rank allreduce
-(low precision and DDA tree), the N=8 x 256 MiB bf16 fused launch, the fp32
-fused launch at 16, 32, 64 and 128 MiB per rank, and the all-to-all-v route,
-row quantize and dequantize at 16,384 x 7168 bf16.
+tree phases at 2 MiB bf16 per rank, the full emulated 8-rank allreduce (low
+precision and DDA tree at 16 MiB, DDA flat at 64 KiB), the N=8 x 256 MiB bf16
+fused launch, the fp32 fused launch at 16, 32, 64 and 128 MiB per rank, and
+the all-to-all-v route, row quantize and dequantize at 16,384 x 7168 bf16.
 """
 from __future__ import annotations
 
@@ -499,6 +499,17 @@ def main():
         kernels["allreduce_emulated_%s_n8_16MiB" % name] = r
         del ar_bufs, ws
     del tree_sets, tree_chunks, tree_out
+    # the small-message allreduce: DDA flat over the 8 emulated ranks at 64 KiB bf16 per rank
+    m64 = inputs.HIDDEN * 4
+    flat_sets = [[torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[4]]
+                 for _ in range(16)]
+    ws_flat = torch.empty(lpc.lpc_allreduce_workspace_bytes(lpc.ALGO_DDA_FLAT, N, m64, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+    r = stats(timer.run(lambda i: lpc.lpc_allreduce_emulated(flat_sets[i % len(flat_sets)], lpc.ALGO_DDA_FLAT,
+                                                             ws_flat), 32), 32)
+    r["what"] = "all 8 ranks' shares in place: one reduce launch and one copy launch"
+    kernels["allreduce_emulated_dda_flat_n8_64KiB"] = r
+    del flat_sets, ws_flat
 
     f_us = kernels["rs_ag_fused_f32_16MiB"]["us"]
     value = fb / (f_us * 1e-6) / 1e9

@@ -125,13 +125,17 @@ lpc_status lpc_allreduce_emulated(void* const bufs[], int nranks, size_t n, lpc_
 
     if (algo == LPC_ALGO_DDA_FLAT) {
         // every rank reduces all buffers into its own workspace output, then
-        // takes it in place
+        // one launch copies each output into its rank's buffer
         const size_t slot = align_up(n * 2);
-        lpc::RankOut outs{};
-        for (int r = 0; r < nranks; ++r) outs.p[r] = ws + r * slot;
+        lpc::RankOut outs{}, back{};
+        lpc::RankBufs slots{};
+        for (int r = 0; r < nranks; ++r) {
+            outs.p[r] = ws + r * slot;
+            slots.p[r] = ws + r * slot;
+            back.p[r] = bufs[r];
+        }
         LPC_TRY_HIP(lpc::launch_dda_flat_ranks(in, nranks, n, outs, stream));
-        for (int r = 0; r < nranks; ++r)
-            LPC_TRY_HIP(hipMemcpyAsync(bufs[r], ws + r * slot, n * 2, hipMemcpyDeviceToDevice, stream));
+        LPC_TRY_HIP(lpc::launch_copy_ranks(slots, nranks, n * 2, back, stream));
         return LPC_OK;
     }
     if (algo == LPC_ALGO_DDA_TREE) {

@@ -1055,6 +1055,25 @@ __global__ __launch_bounds__(kThreads) void gather_copy_ranks_kernel(RankBufs ch
     __builtin_nontemporal_store(v, static_cast<u32x4_t*>(outs.p[blockIdx.z]) + (size_t)p * ngran + g);
 }
 
+// copy `bytes` (even) from src.p[r] to dst.p[r] for every rank r = grid.y:
+// 16-byte granules, and granule `full` takes the tail two bytes at a time
+__global__ __launch_bounds__(kThreads) void copy_ranks_kernel(RankBufs src, size_t bytes, RankOut dst) {
+    const size_t g = granule_id();
+    const size_t full = bytes / 16;
+    const int r = blockIdx.y;
+    if (g < full) {
+        reinterpret_cast<u32x4_t*>(dst.p[r])[g] = reinterpret_cast<const u32x4_t*>(src.p[r])[g];
+    } else if (g == full) {
+        const uint16_t* s = static_cast<const uint16_t*>(src.p[r]);
+        uint16_t* d = static_cast<uint16_t*>(dst.p[r]);
+        for (size_t i = full * 8; i < bytes / 2; ++i) d[i] = s[i];
+    }
+}
+
+hipError_t launch_copy_ranks(const RankBufs& src, int nranks, size_t bytes, const RankOut& dst, hipStream_t stream) {
+    return launch(copy_ranks_kernel, grid_for(bytes / 16 + 1, nranks), dim3(kThreads), 0, stream, src, bytes, dst);
+}
+
 hipError_t launch_dda_tree_ag_ranks(const RankBufs& chunks, int bf16, int nranks, size_t n, const RankOut& outs,
                                     hipStream_t stream) {
     const size_t ngran = n / nranks * (bf16 ? 2 : 4) / 16;

@@ -46,5 +46,6 @@ hipError_t launch_dda_tree_rs_ranks(const RankBufs& b, int bf16, int nranks, siz
                                     hipStream_t stream);
 hipError_t launch_dda_tree_ag_ranks(const RankBufs& chunks, int bf16, int nranks, size_t n, const RankOut& outs,
                                     hipStream_t stream);
+hipError_t launch_copy_ranks(const RankBufs& src, int nranks, size_t bytes, const RankOut& dst, hipStream_t stream);
 
 }  // namespace lpc

@@ -812,6 +812,23 @@ def test_allreduce_emulated(dev, orc, algo, bf16, N):
         assert_same(to_host(bufs[r]), ref, "allreduce %s rank %d" % (lpc.ALGO_NAMES[algo], r))
 
 
+@pytest.mark.parametrize("N,n", [(3, 1001), (8, 8 * 977 + 5), (2, 7), (8, 4096 * 16)])
+def test_allreduce_emulated_dda_flat_ragged(dev, orc, N, n):
+    """DDA flat over emulated ranks at sizes that are not whole 16-byte granules (the
+    copy into the ranks' buffers takes the tail element by element): every buffer
+    equals the oracle's flat reduce."""
+    xs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5)) for r in range(N)]
+    say("allreduce emulated dda_flat ragged N=%d n=%d" % (N, n))
+    bufs = [to_dev(x, dev) for x in xs]
+    ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(lpc.ALGO_DDA_FLAT, N, n, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    lpc.lpc_allreduce_emulated(bufs, lpc.ALGO_DDA_FLAT, ws)
+    torch.cuda.synchronize()
+    ref = orc.dda_flat(xs)
+    for r in range(N):
+        assert_same(to_host(bufs[r]), ref, "dda flat ragged rank %d" % r)
+
+
 def test_allreduce_emulated_dda_flat_rejects_f32(dev):
     """DDA flat reduces bf16 only: fp32 buffers are refused before anything is
     enqueued, and the buffers are left as they were."""
