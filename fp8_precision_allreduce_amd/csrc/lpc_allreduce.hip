@@ -10,10 +10,40 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lpc.h"
 #include "lpc_launch.hpp"
 
+// Scratch of lpc_allreduce_emulated_noalloc: the workspace that
+// lpc_allreduce_emulated takes as an argument, here a file-scope device array.
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to the runtime or a kernel: the name
+// is a host-side stand-in, and the device address comes from
+// hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[LPC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (each GPU holds the array at its own address).
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+lpc_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPC_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return LPC_ERR_HIP;
+    *out = g_scratch_ptr[dev];
+    return LPC_OK;
+}
 
 constexpr size_t kRegionAlign = 256;  // every workspace region starts on a 256-byte boundary
 
@@ -85,6 +115,19 @@ size_t workspace_bytes(lpc_algo algo, int nranks, size_t n, lpc_dtype t) {
         if ((expr) != hipSuccess) return LPC_ERR_HIP;  \
     } while (0)
 
+lpc_status check_bufs(void* const bufs[], int nranks) {
+    for (int r = 0; r < nranks; ++r)
+        if (!bufs[r]) return LPC_ERR_NULL;
+    for (int r = 0; r < nranks; ++r)
+        if (misaligned(bufs[r])) return LPC_ERR_ALIGN;
+    return LPC_OK;
+}
+
+// Every rank's share of the allreduce, one launch per step, with the
+// workspace at `ws` (arguments already checked).
+lpc_status run_allreduce(void* const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo, uint8_t* ws,
+                         hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -112,14 +155,30 @@ lpc_status lpc_allreduce_emulated(void* const bufs[], int nranks, size_t n, lpc_
     LPC_TRY(check_args(algo, nranks, n, t));
     if (n == 0) return LPC_OK;
     if (!bufs || !workspace) return LPC_ERR_NULL;
-    for (int r = 0; r < nranks; ++r)
-        if (!bufs[r]) return LPC_ERR_NULL;
-    for (int r = 0; r < nranks; ++r)
-        if (misaligned(bufs[r])) return LPC_ERR_ALIGN;
+    LPC_TRY(check_bufs(bufs, nranks));
     if (misaligned(workspace)) return LPC_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(algo, nranks, n, t)) return LPC_ERR_SHAPE;
+    return run_allreduce(bufs, nranks, n, t, algo, static_cast<uint8_t*>(workspace), stream);
+}
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+lpc_status lpc_allreduce_emulated_noalloc(void* const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo,
+                                          hipStream_t stream) {
+    LPC_TRY(check_args(algo, nranks, n, t));
+    if (n == 0) return LPC_OK;
+    if (!bufs) return LPC_ERR_NULL;
+    LPC_TRY(check_bufs(bufs, nranks));
+    if (workspace_bytes(algo, nranks, n, t) > LPC_NOALLOC_SCRATCH_BYTES) return LPC_ERR_SCRATCH;
+    void* ws = nullptr;
+    LPC_TRY(scratch_address(&ws));
+    return run_allreduce(bufs, nranks, n, t, algo, static_cast<uint8_t*>(ws), stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+lpc_status run_allreduce(void* const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo, uint8_t* ws,
+                         hipStream_t stream) {
     lpc::RankBufs in{};
     for (int r = 0; r < nranks; ++r) in.p[r] = bufs[r];
 
@@ -173,4 +232,4 @@ lpc_status lpc_allreduce_emulated(void* const bufs[], int nranks, size_t n, lpc_
     return LPC_OK;
 }
 
-}  // extern "C"
+}  // namespace

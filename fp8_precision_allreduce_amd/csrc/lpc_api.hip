@@ -75,6 +75,8 @@ const char* lpc_status_string(lpc_status s) {
         case LPC_ERR_DTYPE: return "LPC_ERR_DTYPE: unknown element type";
         case LPC_ERR_ALIGN: return "LPC_ERR_ALIGN: a pointer is not 16-byte aligned";
         case LPC_ERR_HIP: return "LPC_ERR_HIP: the HIP runtime refused the kernel launch";
+        case LPC_ERR_SCRATCH:
+            return "LPC_ERR_SCRATCH: the call needs more device scratch than the library's static array holds";
     }
     return "unknown lpc_status";
 }

@@ -30,7 +30,8 @@ ALGO_AUTO, ALGO_DDA_FLAT, ALGO_DDA_TREE, ALGO_LOW_PRECISION = 0, 1, 2, 3
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DDA_FLAT: "dda_flat", ALGO_DDA_TREE: "dda_tree",
               ALGO_LOW_PRECISION: "low_precision"}
 STATUS = ["LPC_OK", "LPC_ERR_NULL", "LPC_ERR_SHAPE", "LPC_ERR_RANKS", "LPC_ERR_DTYPE",
-          "LPC_ERR_ALIGN", "LPC_ERR_HIP"]
+          "LPC_ERR_ALIGN", "LPC_ERR_HIP", "LPC_ERR_SCRATCH"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LpcError(RuntimeError):
@@ -58,6 +59,7 @@ SIGNATURES = {
     "lpc_select_algo": [_int, _sz, _int, _int],
     "lpc_allreduce_workspace_bytes": [_int, _int, _sz, _int, ctypes.POINTER(ctypes.c_size_t)],
     "lpc_allreduce_emulated": [_pp, _int, _sz, _int, _int, _vp, _sz, _vp],
+    "lpc_allreduce_emulated_noalloc": [_pp, _int, _sz, _int, _int, _vp],
 }
 
 _lock = threading.Lock()
@@ -267,6 +269,16 @@ def lpc_allreduce_emulated(bufs, algo: int, workspace: torch.Tensor, stream=None
     dt = bufs[0].dtype
     _call("lpc_allreduce_emulated", _ptrs(bufs, "bufs", (dt,), n), N, n, _dtype(bufs[0]), algo,
           _dev(workspace, "workspace", _U8), workspace.numel(), _stream(stream))
+
+
+def lpc_allreduce_emulated_noalloc(bufs, algo: int, stream=None):
+    """lpc_allreduce_emulated with the library's static scratch in place of a workspace
+    (allocates nothing; calls that overlap on one GPU race on the scratch)."""
+    N = len(bufs)
+    n = bufs[0].numel()
+    dt = bufs[0].dtype
+    _call("lpc_allreduce_emulated_noalloc", _ptrs(bufs, "bufs", (dt,), n), N, n, _dtype(bufs[0]), algo,
+          _stream(stream))
 
 
 def lpc_e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None):

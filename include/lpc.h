@@ -34,7 +34,9 @@
  *     scales[], bufs[], ...) are HOST arrays of nranks device pointers, read
  *     during the call and copied into kernel arguments.  The caller owns
  *     every buffer; the library allocates nothing and keeps no state, so
- *     calls are thread-safe.
+ *     calls are thread-safe.  The one exception is
+ *     lpc_allreduce_emulated_noalloc, which works in a static device array
+ *     of the library (see there).
  *   - Work is enqueued on `stream` (NULL: the default stream) and the call
  *     returns without waiting.
  *   - Arguments are checked on the host before anything is enqueued; on any
@@ -71,7 +73,9 @@ typedef enum {
     LPC_ERR_RANKS = 3,  /* nranks outside 1..8, or rank outside 0..nranks-1 */
     LPC_ERR_DTYPE = 4,  /* unknown lpc_dtype */
     LPC_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned */
-    LPC_ERR_HIP = 6     /* the HIP runtime refused the kernel launch */
+    LPC_ERR_HIP = 6,    /* the HIP runtime refused the kernel launch */
+    LPC_ERR_SCRATCH = 7 /* the call needs more than the library's static scratch
+                           (lpc_allreduce_emulated_noalloc only) */
 } lpc_status;
 
 typedef enum {
@@ -277,6 +281,36 @@ lpc_status lpc_allreduce_workspace_bytes(lpc_algo algo, int nranks, size_t n, lp
  * refused launch (LPC_ERR_HIP) may leave the steps before it enqueued.     */
 lpc_status lpc_allreduce_emulated(void *const bufs[], int nranks, size_t n, lpc_dtype t, lpc_algo algo,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the static device scratch of lpc_allreduce_emulated_noalloc (one
+ * copy per GPU the library runs on, held until the process ends). */
+#define LPC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* lpc_allreduce_emulated for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, kernels and results, but no workspace
+ * argument: the workspace is a file-scope device array of
+ * LPC_NOALLOC_SCRATCH_BYTES bytes inside the library.  The call allocates
+ * nothing (no hipMalloc/hipFree); its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress), later calls reuse it.
+ *   - The array belongs to the CURRENT device (hipGetDevice); `stream` must
+ *     be a stream of that device.
+ *   - A workspace need (lpc_allreduce_workspace_bytes) above
+ *     LPC_NOALLOC_SCRATCH_BYTES returns LPC_ERR_SCRATCH, after the other
+ *     argument checks and before any HIP call.  At 8 ranks that allows a
+ *     low-precision allreduce of up to about 7.2M elements per rank, a DDA
+ *     tree of up to 8M fp32 (16M bf16) elements per rank, and DDA flat of up
+ *     to 4M bf16 elements per rank.
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents.  Calls that overlap on one GPU (concurrent
+ *     streams, or threads) race on it: the caller must order them.  Nothing
+ *     in the array needs to start at zero (every byte is written before it
+ *     is read), so the call clears nothing.
+ * Errors: as lpc_allreduce_emulated (no workspace checks), plus
+ * LPC_ERR_SCRATCH; LPC_ERR_HIP also when the device or the array's address
+ * cannot be obtained. */
+lpc_status lpc_allreduce_emulated_noalloc(void *const bufs[], int nranks, size_t n, lpc_dtype t,
+                                          lpc_algo algo, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Codec and library info                                                   */

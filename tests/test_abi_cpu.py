@@ -13,7 +13,7 @@ import pytest
 
 from fp8_precision_allreduce_amd import lpc
 
-OK, NULL, SHAPE, RANKS, DTYPE, ALIGN, HIP = range(7)
+OK, NULL, SHAPE, RANKS, DTYPE, ALIGN, HIP, SCRATCH = range(8)
 A = 0x10000        # a fake 16-byte-aligned device address
 B = 0x10008        # a fake misaligned one
 F32, BF16 = 0, 1
@@ -235,6 +235,37 @@ def test_allreduce_emulated_errors(L):
     assert f(arr(*([A] * 7 + [B])), 8, n, F32, LP, A, ws_need.value, None) == ALIGN
     assert f(bufs, 8, n, F32, LP, B, ws_need.value, None) == ALIGN
     assert f(bufs, 8, n, F32, LP, A, ws_need.value - 1, None) == SHAPE
+
+
+def test_allreduce_emulated_noalloc_errors(L):
+    """The no-allocation variant checks what lpc_allreduce_emulated checks (no workspace
+    arguments), then its static scratch's size; with no GPU visible a call that passes
+    every check fails at the device lookup with LPC_ERR_HIP."""
+    f = L.lpc_allreduce_emulated_noalloc
+    n = 8 * 128 * 4
+    bufs = arr(*([A] * 8))
+    assert f(bufs, 8, n, F32, AUTO, None) == DTYPE
+    assert f(bufs, 8, n, F32, FLAT, None) == DTYPE
+    assert f(bufs, 9, n, F32, LP, None) == RANKS
+    assert f(bufs, 8, n + 128, F32, LP, None) == SHAPE
+    assert f(bufs, 8, 0, F32, LP, None) == OK                    # n == 0: no-op
+    assert f(None, 8, n, F32, LP, None) == NULL
+    assert f(arr(*([A] * 7 + [None])), 8, n, F32, LP, None) == NULL
+    assert f(arr(*([A] * 7 + [B])), 8, n, F32, LP, None) == ALIGN
+    big = 8 * 128 * 8192                                          # about 75 MiB of low-precision workspace
+    need = ctypes.c_size_t(0)
+    assert L.lpc_allreduce_workspace_bytes(LP, 8, big, F32, ctypes.byref(need)) == OK
+    assert need.value > lpc.NOALLOC_SCRATCH_BYTES
+    assert f(bufs, 8, big, F32, LP, None) == SCRATCH
+    assert L.lpc_allreduce_workspace_bytes(TREE, 8, 8 * 8 * 2 ** 18, F32, ctypes.byref(need)) == OK
+    assert need.value <= lpc.NOALLOC_SCRATCH_BYTES
+    assert f(bufs, 8, 8 * 8 * 2 ** 18, F32, TREE, None) == HIP     # passes the checks; no device
+    assert f(bufs, 8, n, F32, LP, None) == HIP
+
+
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define LPC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(lpc.HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == lpc.NOALLOC_SCRATCH_BYTES
 
 
 def test_low_precision_switch_from_env(monkeypatch):
