@@ -12,37 +12,43 @@ One step is rank 0's share of the hot path on that workload:
                          requantized chunks into the 16 MiB fp32 output,
   3. dda_flat_reduce     8 x 64 KiB bf16 -> 64 KiB bf16.
 The other ranks' quantized buffers and reduced chunks are prepared untimed,
-as the peers would have produced them.  Inputs are resident in HBM when the
+as the peers would have produced them.  Inputs are resident in HBM when a
 timed region starts.
 
-Timing.  Every figure comes from HIP events on the stream the kernels run
-on.
-  * Per-kernel mean duration (value, roofline, kernels): a bounded spin
-    kernel is queued first, then the launches of one kernel back to back,
-    with one event before and one after them; the spin keeps the GPU behind
-    the host, so the launches run back to back on the GPU and the host's
-    launch cost stays out.  Mean = elapsed / launches (the pages' protocol:
-    warm-up, then the mean over the measured iterations).
-  * ms_per_step: one HIP graph of K steps, replayed once between two events.
+Timing.  Every figure comes from HIP events on the stream the kernels run on.
+  * Per-kernel durations (value, roofline, kernels): the pages' protocol,
+    warm-up launches then the mean over the measured launches, done as
+    --batches batches.  Each batch: a read-only pass over 1 GiB (so that no
+    batch starts with the previous one's data in the 256 MB Infinity Cache),
+    a bounded spin kernel that keeps the GPU behind the host, --batch-warmup
+    untimed launches, then --launches launches back to back between two
+    events.  mean_us = mean over all measured launches; median_us, min_us and
+    max_us are over the batch means.
+  * ms_per_step: the K steps launched back to back behind a spin kernel,
+    between two events (synchronized before and after).  The same timing
+    with one kernel left out of every step gives each kernel's marginal cost
+    inside the step (step_parts).
 The timed launches cycle through enough buffer copies (--sets) that the
-256 MB Infinity Cache cannot hold them, so the kernels stream from HBM; the
-256 MiB and all-to-all-v launches alternate between two copies of their
-buffers.  The cache-warm DDA figure is reported beside the cold one.
+Infinity Cache cannot hold them, so the kernels stream from HBM.
 
 value = algorithmic bytes of one fused RS+AG launch / its mean duration
-(GB/s).  roofline compares it with the 8 TB/s HBM peak; traffic is the HBM
-byte count per launch from rocprofv3 counters (profiles/traffic.json), null
-when those counters were taken on other kernel sources.  For context the
-roofline object also carries the mean duration of an empty launch timed the
-same way (empty_launch_us) and the rate of the fused launch beyond it.
-cpu_baseline is the CPU oracle on a bounded sample of the same share.
+(GB/s).  The roofline object compares it with the 8 TB/s HBM peak and with
+two references timed the same way in the same run: a plain streaming kernel
+moving the same bytes at the same read:write mix (lpc_measure_stream, the
+practical ceiling), and an empty launch of the fused kernel's shape
+(lpc_measure_empty: its grid and argument size, the fixed cost of that
+launch).  traffic is the HBM byte count per launch from rocprofv3 counters
+(profiles/traffic.json), null when those counters were taken on other kernel
+sources.  cpu_baseline is the CPU oracle on a bounded sample of the same
+share, on one host core.
 
-Extra per-kernel lines (not part of the step): the unfused reduce-scatter
-and all-gather, the one-quantization low-precision reduce-scatter, the DDA
-tree phases at 2 MiB bf16 per rank, the full emulated 8-rank allreduce (low
-precision and DDA tree at 16 MiB, DDA flat at 64 KiB), the N=8 x 256 MiB bf16
-fused launch, the fp32 fused launch at 16, 32, 64 and 128 MiB per rank, and
-the all-to-all-v route, row quantize and dequantize at 16,384 x 7168 bf16.
+Extra per-kernel lines (not part of the step): the fused launch at rank 7,
+the unfused reduce-scatter and all-gather, the one-quantization
+low-precision reduce-scatter, the DDA tree phases at 2 MiB bf16 per rank,
+the emulated 8-rank allreduce (low precision and DDA tree at 16 MiB, DDA
+flat at 64 KiB), the N=8 x 256 MiB bf16 fused launch and quantize, the fp32
+fused launch at 16, 32, 64 and 128 MiB per rank, and the all-to-all-v route,
+row quantize and dequantize at 16,384 x 7168 bf16.
 """
 from __future__ import annotations
 
@@ -63,6 +69,12 @@ HBM_PEAK_GBPS = 8000.0
 BLOCK = 128
 NRANKS = 8
 MALL_BYTES = 256 * 2 ** 20
+EVICT_BYTES = 2 ** 30
+THREADS = 256
+# kernel-argument bytes of the fused kernel: two RankCodes (8 code and 8 scale
+# pointers each), rank, C, and the chunk-code, chunk-scale and output pointers
+FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 3 * 8
+QUANT_KERNARG = 4 * 8                       # x, granule count, codes, scales
 
 
 # -- algorithmic bytes (every byte read and written, scales included) -------------
@@ -71,9 +83,17 @@ def chunk_bytes(C: int) -> int:
     return C + C // BLOCK * 4                     # codes + scales of one chunk
 
 
-def fused_bytes(n: int, N: int, out_size: int) -> int:
+def fused_read_bytes(n: int, N: int) -> int:
     C = n // N
-    return N * chunk_bytes(C) + chunk_bytes(C) + (N - 1) * chunk_bytes(C) + n * out_size
+    return N * chunk_bytes(C) + (N - 1) * chunk_bytes(C)
+
+
+def fused_write_bytes(n: int, N: int, out_size: int) -> int:
+    return chunk_bytes(n // N) + n * out_size
+
+
+def fused_bytes(n: int, N: int, out_size: int) -> int:
+    return fused_read_bytes(n, N) + fused_write_bytes(n, N, out_size)
 
 
 def rs_bytes(n: int, N: int) -> int:
@@ -93,7 +113,7 @@ def dda_bytes(n: int, N: int) -> int:
     return (N + 1) * n * 2
 
 
-KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every kernel's device code lives in these two
+KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every path kernel's device code lives in these two
 
 
 def source_digest() -> str:
@@ -124,6 +144,21 @@ def traffic_from_profiles(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """(model name, CPUs this process may run on, CPUs in the machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, usable, os.cpu_count()
+
+
 def cpu_baseline(xs, min_seconds: float):
     """The CPU oracle (single-threaded C) on a bounded sample of the same workload:
     rank 0's reduce-scatter chunk + all-gather dequant, repeated for ~min_seconds."""
@@ -146,55 +181,27 @@ def cpu_baseline(xs, min_seconds: float):
         if el >= min_seconds:
             break
     per = el / reps
+    model, usable, total = host_cpu()
     return {
         "value": round(fused_bytes(n, N, 4) / per / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": "rank 0's reduce-scatter chunk + all-gather dequant of the N=8 x 16 MiB fp32 "
-                  "workload (same algorithmic bytes as one fused launch), %d repetitions in %.1f s, "
-                  "single-threaded C oracle" % (reps, el),
+                  "workload: the two steps the fused launch does, over the same algorithmic bytes; %d "
+                  "repetitions in %.1f s, single-threaded C oracle" % (reps, el),
+        "host_cores": usable,
+        "host_cpus_total": total,
+        "cpu_model": model,
     }
 
 
-class GraphTimer:
-    """Capture `count` calls of fn(i) into one HIP graph on a side stream; time replays."""
-
-    def __init__(self, torch, fn, count: int):
-        self.torch = torch
-        self.count = count
-        self.stream = torch.cuda.Stream()
-        self.stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(self.stream):
-            fn(0)                       # one eager call on the capture stream before capture
-        torch.cuda.synchronize()
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph, stream=self.stream):
-            for i in range(count):
-                fn(i)
-        torch.cuda.synchronize()
-
-    def replay_us(self, reps: int = 1) -> float:
-        """Mean device time per captured call over `reps` replays.  A replay runs on
-        the current stream, so the events are recorded there."""
-        torch = self.torch
-        stream = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            self.graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * self.count)
-
-
 class BatchTimer:
-    """Mean device time per launch of a batch queued behind a spin kernel."""
+    """Launches queued behind a bounded spin kernel, timed with events on the launch stream."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, evict=None):
         self.torch = torch
+        self.evict = evict
         torch.cuda._sleep(1000)                  # load the spin kernel before calibrating it
         torch.cuda.synchronize()
         cycles = 20_000_000
@@ -207,46 +214,85 @@ class BatchTimer:
         torch.cuda.synchronize()
         self.cycles_per_us = cycles / max(e0.elapsed_time(e1) * 1e3, 1.0)
 
-    def run(self, fn, count: int):
-        """Launch fn(0..count-1) back to back; returns (mean us per launch, GPU was never idle).
-        If the host's enqueueing outlasted the spin, the batch is run again with a longer spin
+    def batch(self, fn, base: int, warm: int, count: int):
+        """fn(base .. base+warm-1) untimed, then fn(base+warm .. base+warm+count-1) between two
+        events, all behind one spin.  Returns (mean us per timed launch, the GPU was never idle).
+        If the host's enqueueing outlasted the spin, the batch runs again with a longer spin
         (at most twice)."""
         torch = self.torch
         torch.cuda.synchronize()
-        t0 = time.perf_counter()                 # host cost per launch, from a short untimed batch
+        t0 = time.perf_counter()                 # host cost per launch, from a short untimed run
         for i in range(min(count, 8)):
-            fn(i)
+            fn(base + i)
         host_us = (time.perf_counter() - t0) * 1e6 / min(count, 8)
         torch.cuda.synchronize()
-        spin_us = host_us * count * 2.0 + 1000.0
+        spin_us = host_us * (warm + count) * 2.0 + 1000.0
         for _ in range(3):
+            if self.evict is not None:
+                self.evict()
             es = torch.cuda.Event(enable_timing=True)
+            ew = torch.cuda.Event(enable_timing=True)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             es.record()
             torch.cuda._sleep(int(self.cycles_per_us * spin_us))
-            e0.record()
+            ew.record()
             t1 = time.perf_counter()
+            for i in range(warm):
+                fn(base + i)
+            e0.record()
             for i in range(count):
-                fn(i)
-            enqueue_us = (time.perf_counter() - t1) * 1e6
+                fn(base + warm + i)
             e1.record()
+            enqueue_us = (time.perf_counter() - t1) * 1e6
             torch.cuda.synchronize()
-            # the spin started no later than the host began enqueueing; it must outlast the enqueueing
-            fed = es.elapsed_time(e0) * 1e3 > enqueue_us
+            # the spin started no later than the host began enqueueing; if it outlasted all of the
+            # enqueueing, every launch was queued before the GPU reached it
+            fed = es.elapsed_time(ew) * 1e3 > enqueue_us
             if fed:
                 break
             spin_us = enqueue_us * 3.0 + 1000.0
         return e0.elapsed_time(e1) * 1e3 / count, fed
 
+    def measure(self, fn, batches: int, count: int, warm: int, nbytes=None) -> dict:
+        """`batches` batches of `warm` + `count` launches; mean over all timed launches, and
+        median / min / max over the batch means."""
+        per, fed_all, base = [], True, 0
+        for _ in range(batches):
+            us, fed = self.batch(fn, base, warm, count)
+            base += warm + count
+            per.append(us)
+            fed_all = fed_all and fed
+        d = {"us": round(float(np.mean(per)), 3), "median_us": round(float(np.median(per)), 3),
+             "min_us": round(min(per), 3), "max_us": round(max(per), 3),
+             "batch_us": [round(u, 3) for u in per], "batches": batches, "launches_per_batch": count,
+             "warmup_per_batch": warm, "gpu_fed": bool(fed_all)}
+        if nbytes:
+            d["bytes"] = nbytes
+            d["gbps"] = round(nbytes / d["us"] / 1e3, 1)
+        return d
 
-def stats(res, count, nbytes=None):
-    us, fed = res
-    d = {"us": round(us, 3), "launches": count, "gpu_fed": bool(fed)}
-    if nbytes:
-        d["bytes"] = nbytes
-        d["gbps"] = round(nbytes / us / 1e3, 1)
-    return d
+    def sequence(self, fn, count: int) -> float:
+        """fn(0 .. count-1) back to back behind one spin, between two events (synchronized
+        before and after); mean device microseconds per call."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(min(count, 4)):
+            fn(i)
+        host_us = (time.perf_counter() - t0) * 1e6 / min(count, 4)
+        torch.cuda.synchronize()
+        if self.evict is not None:
+            self.evict()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(self.cycles_per_us * (host_us * count * 2.0 + 1000.0)))
+        e0.record()
+        for i in range(count):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / count
 
 
 class Arena:
@@ -255,9 +301,8 @@ class Arena:
     The N emulated ranks' buffers share one GPU's HBM, which a real rank's
     peers (each in its own GPU's memory) do not.  Allocated one tensor at a
     time, the fused kernel's time at 16 MiB depended on where the allocator
-    placed them: 4.88 to 5.59 us per launch across placements and boxes, and
-    up to 10% apart between two placements on one box.  Packed into one
-    allocation it measured 4.85 to 5.01 us on the same boxes."""
+    placed them (4.88 to 5.59 us per launch across placements and boxes);
+    packed into one allocation it measured 4.85 to 5.01 us on the same boxes."""
 
     ALIGN = 4096
 
@@ -274,18 +319,43 @@ class Arena:
         return t
 
 
+def fused_layout(n: int, N: int, out_size: int):
+    """Byte sizes, in order, of one fused-launch buffer set: every rank's codes and scales,
+    every rank's requantized chunk, the own chunk's output, and the output."""
+    C = n // N
+    return [n, n // BLOCK * 4] * N + [C, C // BLOCK * 4] * (N + 1) + [n * out_size]
+
+
+def fused_set(torch, dev, n: int, N: int, out_dtype):
+    """One buffer set of the fused launch carved from one allocation (fused_layout's order)."""
+    C = n // N
+    u8, f32 = torch.uint8, torch.float32
+    a = Arena(torch, dev, fused_layout(n, N, torch.empty((), dtype=out_dtype).element_size()))
+    b = dict(codes=[], scales=[], cc=[], cs=[])
+    for _ in range(N):
+        b["codes"].append(a.take(n, u8))
+        b["scales"].append(a.take(n // BLOCK, f32))
+    for _ in range(N):
+        b["cc"].append(a.take(C, u8))
+        b["cs"].append(a.take(C // BLOCK, f32))
+    b["oc"], b["os"], b["out"] = a.take(C, u8), a.take(C // BLOCK, f32), a.take(n, out_dtype)
+    b["arena"] = a
+    return b
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batches", type=int, default=5, help="timed batches per kernel")
+    ap.add_argument("--launches", type=int, default=100, help="timed launches per batch (the pages' 100)")
+    ap.add_argument("--batch-warmup", type=int, default=10, help="untimed launches before each batch (the pages' 10)")
     ap.add_argument("--sets", type=int, default=16, help="buffer copies of the 16 MiB workload cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-kernel lines outside the step (256 MiB bf16, fused by size, all-to-all-v)")
-    ap.add_argument("--dda-sets", type=int, default=0,
-                    help="DDA buffer sets cycled through (0: enough to exceed the 256 MB cache)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 64 MiB device copy (calibration for counter runs)")
     args = ap.parse_args()
@@ -305,239 +375,252 @@ def main():
     lpc.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    u8, f32 = torch.uint8, torch.float32
     N = NRANKS
     n = inputs.WORKLOADS[inputs.LP_16MIB]["n"]
     C = n // N
+    B, L, WB = args.batches, args.launches, args.batch_warmup
     log("generating workload: N=%d x %d fp32 per rank" % (N, n))
     xs_host = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(N)]
 
     # -- untimed setup: every rank's quantized buffer and reduced chunk ------------------
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
-    codes = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(N)]
-    scales = [torch.empty(n // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    codes = [torch.empty(n, dtype=u8, device=dev) for _ in range(N)]
+    scales = [torch.empty(n // BLOCK, dtype=f32, device=dev) for _ in range(N)]
     for r in range(N):
         lpc.lpc_quantize_fp8(xs[r], codes[r], scales[r])
-    cc = [torch.empty(C, dtype=torch.uint8, device=dev) for _ in range(N)]
-    cs = [torch.empty(C // BLOCK, dtype=torch.float32, device=dev) for _ in range(N)]
+    cc = [torch.empty(C, dtype=u8, device=dev) for _ in range(N)]
+    cs = [torch.empty(C // BLOCK, dtype=f32, device=dev) for _ in range(N)]
     for r in range(N):
         lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
-    out_ref = torch.empty(n, dtype=torch.float32, device=dev)
+    out_ref = torch.empty(n, dtype=f32, device=dev)
     lpc.lpc_allgather_dequant(cc, cs, out_ref)
     torch.cuda.synchronize()
 
+    # fused-launch sets (only what the fused launch touches) and quantize sets, each cycled
     S = max(1, args.sets)
     sets = []
-    u8, f32 = torch.uint8, torch.float32
     for _ in range(S):
-        a = Arena(torch, dev, [n * 4] + [n, n // BLOCK * 4] * N + [C, C // BLOCK * 4] * (2 * N + 1) + [n * 4])
-        b = dict(x=a.take(n, f32))
-        b["codes"], b["scales"] = [], []
-        for r in range(N):
-            b["codes"].append(a.take(n, u8))
-            b["scales"].append(a.take(n // BLOCK, f32))
-        b["peer_c"], b["peer_s"], b["all_c"], b["all_s"] = [None], [None], [], []
-        for r in range(N):
-            if r > 0:
-                b["peer_c"].append(a.take(C, u8))
-                b["peer_s"].append(a.take(C // BLOCK, f32))
-            b["all_c"].append(a.take(C, u8))
-            b["all_s"].append(a.take(C // BLOCK, f32))
-        b["own_c"], b["own_s"], b["out"] = a.take(C, u8), a.take(C // BLOCK, f32), a.take(n, f32)
-        b["x"].copy_(xs[0])
+        b = fused_set(torch, dev, n, N, f32)
         for r in range(N):
             b["codes"][r].copy_(codes[r])
             b["scales"][r].copy_(scales[r])
-            b["all_c"][r].copy_(cc[r])
-            b["all_s"][r].copy_(cs[r])
-            if r > 0:
-                b["peer_c"][r].copy_(cc[r])
-                b["peer_s"][r].copy_(cs[r])
+            b["cc"][r].copy_(cc[r])
+            b["cs"][r].copy_(cs[r])
+        b["rs_out"] = torch.empty(C, dtype=f32, device=dev)
         sets.append(b)
-    set_bytes = sum(t.numel() * t.element_size() for b in sets[:1] for k, v in b.items()
-                    for t in (v if isinstance(v, list) else [v]) if t is not None)
+    qsets = []
+    for _ in range(S):
+        a = Arena(torch, dev, [n * 4, n, n // BLOCK * 4])
+        q = dict(x=a.take(n, f32), codes=a.take(n, u8), scales=a.take(n // BLOCK, f32), arena=a)
+        q["x"].copy_(xs[0])
+        qsets.append(q)
+    set_bytes = sum(fused_layout(n, N, 4))
 
     # DDA flat sets: 8 ranks x (hidden 8192 x T) bf16 + output, enough to exceed the cache
     dda_host = {T: inputs.dda_buffers(T) for T in inputs.DDA_TOKENS}
 
-    def dda_sets(T, count):
+    def dda_sets(T):
         m = dda_host[T][0].size
+        count = max(64, -(-2 * MALL_BYTES // dda_bytes(m, N)))
         pool = torch.empty((count, N + 1, m), dtype=torch.bfloat16, device=dev)
         src = torch.stack([torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[T]])
         pool[:, :N].copy_(src.unsqueeze(0).expand(count, N, m))
         return pool
 
-    def dda_cold_count(T):
-        if args.dda_sets > 0:
-            return args.dda_sets
-        m = dda_host[T][0].size
-        return max(64, -(-2 * MALL_BYTES // dda_bytes(m, N)))
-
-    pools = {T: dda_sets(T, dda_cold_count(T)) for T in inputs.DDA_TOKENS}
+    pools = {T: dda_sets(T) for T in inputs.DDA_TOKENS}
+    evict_buf = torch.zeros(EVICT_BYTES, dtype=u8, device=dev)
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
+
+    def evict():
+        # a read-only pass over 1 GiB: later launches find none of their data in the Infinity Cache
+        lpc.lpc_measure_stream(evict_buf, EVICT_BYTES, sink, 16)
 
     # -- the kernels --------------------------------------------------------------------------
     def quantize(i):
-        b = sets[i % S]
-        lpc.lpc_quantize_fp8(b["x"], b["codes"][0], b["scales"][0])
+        q = qsets[i % S]
+        lpc.lpc_quantize_fp8(q["x"], q["codes"], q["scales"])
 
-    def fused(i):
-        b = sets[i % S]
-        lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["own_c"], b["own_s"], b["peer_c"], b["peer_s"],
-                            b["out"])
+    def fused_at(rank):
+        def f(i):
+            b = sets[i % S]
+            peers_c = [None if p == rank else b["cc"][p] for p in range(N)]
+            peers_s = [None if p == rank else b["cs"][p] for p in range(N)]
+            lpc.lpc_rs_ag_fused(b["codes"], b["scales"], rank, b["oc"], b["os"], peers_c, peers_s, b["out"])
+        return f
+
+    fused = fused_at(0)
 
     def rs_chunk(i):
         b = sets[i % S]
-        lpc.lpc_reduce_scatter_chunk(b["codes"], b["scales"], 0, b["own_c"], b["own_s"])
+        lpc.lpc_reduce_scatter_chunk(b["codes"], b["scales"], 0, b["oc"], b["os"])
 
     def allgather(i):
         b = sets[i % S]
-        lpc.lpc_allgather_dequant(b["all_c"], b["all_s"], b["out"])
+        lpc.lpc_allgather_dequant(b["cc"], b["cs"], b["out"])
+
+    def lp_rs(i):
+        b = sets[i % S]
+        lpc.lpc_reduce_scatter(b["codes"], b["scales"], 0, b["rs_out"])
 
     def dda(T, i):
         pool = pools[T]
         k = i % pool.shape[0]
         lpc.dda_flat_reduce([pool[k, p] for p in range(N)], pool[k, N])
 
-    def step(i):
-        quantize(i)
-        fused(i)
-        dda(4, i)
+    def step(i, parts="qfd"):
+        if "q" in parts:
+            quantize(i)
+        if "f" in parts:
+            fused(i)
+        if "d" in parts:
+            dda(4, i)
 
-    # -- warmup (eager), then graph capture of the K steps -------------------------------------------
+    # -- warmup, then the timed region: exactly K steps ---------------------------------------------
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    log("capturing graphs (%d steps)" % K)
-    g_step = GraphTimer(torch, step, K)
-    g_step.replay_us(1)                     # warm replay, untimed
-
-    # -- timed region: exactly K steps ------------------------------------------------------------------
-    torch.cuda.synchronize()
+    timer = BatchTimer(torch, evict)
+    log("timing %d steps" % K)
     t_wall = time.perf_counter()
-    step_us = g_step.replay_us(1)
+    step_us = timer.sequence(step, K)
     wall_s = time.perf_counter() - t_wall
     total_ms = step_us * K / 1e3
+    # each kernel's marginal cost inside the step: the same K steps with that kernel left out
+    step_parts = {"step_us": round(step_us, 3)}
+    for part, name in (("fd", "quantize"), ("qd", "rs_ag_fused"), ("qf", "dda_flat")):
+        t = timer.sequence(lambda i, part=part: step(i, part), K)
+        step_parts["without_%s_us" % name] = round(t, 3)
+        step_parts["%s_in_step_us" % name] = round(step_us - t, 3)
 
-    # -- per-kernel mean durations, each batch after a cache-evicting replay ------------------------------
-    timer = BatchTimer(torch)
-    L = max(K, 2 * S)
-
-    def timed(fn, count, nbytes=None):
-        g_step.replay_us(1)                 # >1 GB of other traffic: the batch starts cache-cold
-        return stats(timer.run(fn, count), count, nbytes)
-
+    # -- per-kernel durations ----------------------------------------------------------------------
+    log("per-kernel batches (%d x (%d + %d launches))" % (B, WB, L))
     fb = fused_bytes(n, N, 4)
     kernels = {
-        "rs_ag_fused_f32_16MiB": timed(fused, L, fb),
-        "quantize_f32_16MiB": timed(quantize, L, quantize_bytes(n, 4)),
-        "reduce_scatter_chunk_16MiB": timed(rs_chunk, L, rs_bytes(n, N)),
-        "allgather_dequant_f32_16MiB": timed(allgather, L, ag_bytes(n, N, 4)),
+        "rs_ag_fused_f32_16MiB": timer.measure(fused, B, L, WB, fb),
+        "quantize_f32_16MiB": timer.measure(quantize, B, L, WB, quantize_bytes(n, 4)),
+        "reduce_scatter_chunk_16MiB": timer.measure(rs_chunk, B, L, WB, rs_bytes(n, N)),
+        "allgather_dequant_f32_16MiB": timer.measure(allgather, B, L, WB, ag_bytes(n, N, 4)),
+        "lp_reduce_scatter_f32_16MiB": timer.measure(lp_rs, B, L, WB, N * chunk_bytes(C) + C * 4),
     }
+    hk = kernels["rs_ag_fused_f32_16MiB"]
+    # the same launch at the last rank (its chunk at the end of every buffer, its peers 0..6)
+    hk["rank%d_us" % (N - 1)] = timer.measure(fused_at(N - 1), 2, L, WB)["us"]
+    hk["in_step_us"] = step_parts["rs_ag_fused_in_step_us"]
+
+    # references in the same run: plain streaming kernels at the fused and quantize mixes, an
+    # empty launch of each kernel's shape, and a minimal empty launch
+    pool_src = [torch.ones(32 * 2 ** 20, dtype=u8, device=dev) for _ in range(S)]
+    pool_dst = [torch.empty(32 * 2 ** 20, dtype=u8, device=dev) for _ in range(S)]
+
+    def stream(rb, wb):
+        def f(i):
+            lpc.lpc_measure_stream(pool_src[i % S], rb, pool_dst[i % S], wb)
+        return f
+
+    fr, fw = fused_read_bytes(n, N), fused_write_bytes(n, N, 4)
+    qr, qw = n * 4, n + n // BLOCK * 4
+    ceil_f = timer.measure(stream(fr, fw), B, L, WB, fr + fw)
+    ceil_q = timer.measure(stream(qr, qw), B, L, WB, qr + qw)
+    fgrid = (-(-C // (4 * THREADS)), N - 1)
+    qgrid = (-(-n // (16 * THREADS)), 1)
+    floor_f = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_KERNARG, sink),
+                            B, L, WB)
+    floor_q = timer.measure(lambda i: lpc.lpc_measure_empty(qgrid[0], qgrid[1], THREADS, QUANT_KERNARG, sink),
+                            B, L, WB)
+    empty = timer.measure(lambda i: lpc.lpc_measure_empty(1, 1, 64, 16, sink), B, L, WB)
+    for k, c, fl, grid, ka in (("rs_ag_fused_f32_16MiB", ceil_f, floor_f, fgrid, FUSED_KERNARG),
+                               ("quantize_f32_16MiB", ceil_q, floor_q, qgrid, QUANT_KERNARG)):
+        kernels[k]["ceiling_us"] = c["us"]
+        kernels[k]["ceiling_gbps"] = c["gbps"]
+        kernels[k]["frac_of_ceiling"] = round(c["us"] / kernels[k]["us"], 4)
+        kernels[k]["floor_us"] = fl["us"]
+        kernels[k]["floor_shape"] = "%dx%d workgroups of %d lanes, %d argument bytes" % (grid[0], grid[1], THREADS, ka)
+    kernels["stream_ceiling_fused_mix"] = ceil_f
+    kernels["stream_ceiling_quantize_mix"] = ceil_q
+    kernels["empty_launch_min"] = empty
+    del pool_src, pool_dst
+
     dda_res = {}
     for T in inputs.DDA_TOKENS:
         m = dda_host[T][0].size
-        cnt = min(K, pools[T].shape[0])
-        r = timed(lambda i, T=T: dda(T, i), cnt, dda_bytes(m, N))
-        r["buffer_sets"] = cnt
+        r = timer.measure(lambda i, T=T: dda(T, i), B, L, WB, dda_bytes(m, N))
+        r["buffer_sets"] = pools[T].shape[0]
         dda_res["%dKiB" % (m * 2 // 1024)] = r
-    warm = stats(timer.run(lambda i: dda(4, i % 4), K), K)
-    dda_res["64KiB"]["us_warm"] = warm["us"]
-    # the same batch of launches of a kernel that does nothing (one lane, no memory): the fixed cost
-    # every launch above pays before it moves a byte
-    floor_us = timer.run(lambda i: torch.cuda._sleep(0), L)[0]
+    dda_res["64KiB"]["us_warm"] = timer.measure(lambda i: dda(4, i % 4), B, L, WB)["us"]
+    dda_res["64KiB"]["in_step_us"] = step_parts["dda_flat_in_step_us"]
 
-    # -- the same two headline kernels as graph replays (back to back inside one graph) --------------------
-    g_fused = GraphTimer(torch, fused, L)
-    g_dda = GraphTimer(torch, lambda i: dda(4, i), pools[4].shape[0])
-    g_fused.replay_us(1)
-    g_dda.replay_us(1)
-    kernels["rs_ag_fused_f32_16MiB"]["graph_replay_us"] = round(g_fused.replay_us(3), 3)
-    dda_res["64KiB"]["graph_replay_us"] = round(g_dda.replay_us(3), 3)
-
-    # -- every launch and replay left the eager result in place --------------------------------------------
+    # -- every launch left the eager result in place (the last launches on the fused sets were the
+    # rank N-1 ones, so each set holds rank N-1's requantized chunk) ------------------------------------
     for b in sets:
-        assert torch.equal(b["own_c"], cc[0]), "reduced chunk differs from the eager result"
-        assert torch.equal(b["own_s"].view(torch.int32), cs[0].view(torch.int32)), "chunk scales differ"
+        assert torch.equal(b["oc"], cc[N - 1]), "reduced chunk differs from the eager result"
+        assert torch.equal(b["os"].view(torch.int32), cs[N - 1].view(torch.int32)), "chunk scales differ"
         assert torch.equal(b["out"].view(torch.int32), out_ref.view(torch.int32)), "output differs"
-        assert torch.equal(b["codes"][0], codes[0]), "quantized buffer differs"
+    for q in qsets:
+        assert torch.equal(q["codes"], codes[0]), "quantized buffer differs"
     for T in inputs.DDA_TOKENS:
         pool = pools[T]
         ref = torch.empty_like(pool[0, N])
         lpc.dda_flat_reduce([pool[0, p] for p in range(N)], ref)
-        written = pool[:min(K, pool.shape[0]), N]
+        written = pool[:min(pool.shape[0], B * (WB + L)), N]     # the sets the timed batches used
         assert torch.equal(written.view(torch.int16), ref.view(torch.int16).expand_as(written)), \
             "DDA flat output differs"
     torch.cuda.synchronize()
 
-    # -- next rows: one-quantization reduce-scatter, DDA tree, the emulated 8-rank allreduce ---------------
-    def lp_rs(i):
-        b = sets[i % S]
-        lpc.lpc_reduce_scatter(b["codes"], b["scales"], 0, b["rs_out"])
-
-    for b in sets:
-        b["rs_out"] = torch.empty(C, dtype=torch.float32, device=dev)
-    kernels["lp_reduce_scatter_f32_16MiB"] = timed(lp_rs, L, N * chunk_bytes(C) + C * 4)
+    # -- next rows: DDA tree, the emulated 8-rank allreduce ----------------------------------------------
     nt = 8 * 2 ** 20 // 16 * 2                            # 2 MiB of bf16 per rank
     tree_sets = [[torch.randn(nt, device=dev).to(torch.bfloat16) for _ in range(N)] for _ in range(S)]
     tree_chunks = [[torch.empty(nt // N, dtype=torch.bfloat16, device=dev) for _ in range(N)] for _ in range(S)]
     tree_out = [torch.empty(nt, dtype=torch.bfloat16, device=dev) for _ in range(S)]
-    kernels["dda_tree_rs_bf16_2MiB"] = timed(
-        lambda i: lpc.dda_tree_reduce_scatter(tree_sets[i % S], 0, tree_chunks[i % S][0]), L,
+    kernels["dda_tree_rs_bf16_2MiB"] = timer.measure(
+        lambda i: lpc.dda_tree_reduce_scatter(tree_sets[i % S], 0, tree_chunks[i % S][0]), B, L, WB,
         N * (nt // N) * 2 + (nt // N) * 2)
-    kernels["dda_tree_ag_bf16_2MiB"] = timed(
-        lambda i: lpc.dda_tree_allgather(tree_chunks[i % S], tree_out[i % S]), L, nt * 2 * 2)
-    for algo, name, dt in ((lpc.ALGO_LOW_PRECISION, "low_precision", torch.float32),
-                           (lpc.ALGO_DDA_TREE, "dda_tree", torch.float32)):
-        ar_bufs = [[b["out"]] + [torch.empty(n, dtype=dt, device=dev) for _ in range(N - 1)] for b in sets[:4]]
+    kernels["dda_tree_ag_bf16_2MiB"] = timer.measure(
+        lambda i: lpc.dda_tree_allgather(tree_chunks[i % S], tree_out[i % S]), B, L, WB, nt * 2 * 2)
+    del tree_sets, tree_chunks, tree_out
+    for algo, name, dt in ((lpc.ALGO_LOW_PRECISION, "low_precision", f32),
+                           (lpc.ALGO_DDA_TREE, "dda_tree", f32)):
+        ar_bufs = [[torch.empty(n, dtype=dt, device=dev) for _ in range(N)] for _ in range(4)]
         for bl in ar_bufs:
             for t in bl:
                 t.copy_(xs[0])
-        ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, n, dt), dtype=torch.uint8, device=dev)
-        r = stats(timer.run(lambda i: lpc.lpc_allreduce_emulated(ar_bufs[i % len(ar_bufs)], algo, ws), 8), 8)
+        ws = torch.empty(lpc.lpc_allreduce_workspace_bytes(algo, N, n, dt), dtype=u8, device=dev)
+        r = timer.measure(lambda i: lpc.lpc_allreduce_emulated(ar_bufs[i % len(ar_bufs)], algo, ws), 3, 8, 2)
         r["what"] = "all 8 ranks' shares in place, one launch per step"
         kernels["allreduce_emulated_%s_n8_16MiB" % name] = r
         del ar_bufs, ws
-    del tree_sets, tree_chunks, tree_out
     # the small-message allreduce: DDA flat over the 8 emulated ranks at 64 KiB bf16 per rank
     m64 = inputs.HIDDEN * 4
     flat_sets = [[torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[4]]
                  for _ in range(16)]
     ws_flat = torch.empty(lpc.lpc_allreduce_workspace_bytes(lpc.ALGO_DDA_FLAT, N, m64, torch.bfloat16),
-                          dtype=torch.uint8, device=dev)
-    r = stats(timer.run(lambda i: lpc.lpc_allreduce_emulated(flat_sets[i % len(flat_sets)], lpc.ALGO_DDA_FLAT,
-                                                             ws_flat), 32), 32)
+                          dtype=u8, device=dev)
+    r = timer.measure(lambda i: lpc.lpc_allreduce_emulated(flat_sets[i % len(flat_sets)], lpc.ALGO_DDA_FLAT,
+                                                           ws_flat), B, 32, 4)
     r["what"] = "all 8 ranks' shares in place: one reduce launch and one copy launch"
     kernels["allreduce_emulated_dda_flat_n8_64KiB"] = r
     del flat_sets, ws_flat
 
-    f_us = kernels["rs_ag_fused_f32_16MiB"]["us"]
+    f_us = hk["us"]
     value = fb / (f_us * 1e-6) / 1e9
-    del g_step, g_fused, g_dda, pools
+    del pools
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
-    # -- extra per-kernel lines: 256 MiB bf16 per rank, all-to-all-v rows ------------------------------
+    # -- extra per-kernel lines: 256 MiB bf16 per rank, fused by size, all-to-all-v rows -------------------
     if not args.no_extra:
-        log("256 MiB bf16 per rank (device-generated) and all-to-all-v rows")
+        log("256 MiB bf16 per rank (device-generated), fused by size, all-to-all-v rows")
         # Two copies of each large workload, used in turn: one copy (about 1.4 GiB for the 256 MiB
-        # fused launch) already exceeds the 256 MB Infinity Cache, but a kernel relaunched on the
-        # same buffers still finds part of them there (quantize bf16: 58 against 70 us).
+        # fused launch) already exceeds the 256 MB Infinity Cache.
         COPIES = 2
         n4 = inputs.WORKLOADS[inputs.LP_256MIB_BF16]["n"]
         C4 = n4 // N
         sets4 = []
         for k in range(COPIES):
-            a4 = Arena(torch, dev, [n4 * 2] + [n4, n4 // BLOCK * 4] * N + [C4, C4 // BLOCK * 4] * (N + 1) + [n4 * 2])
-            b4 = dict(x=a4.take(n4, torch.bfloat16), codes=[], scales=[], cc=[], cs=[])
-            for r in range(N):
-                b4["codes"].append(a4.take(n4, torch.uint8))
-                b4["scales"].append(a4.take(n4 // BLOCK, torch.float32))
-            for r in range(N):
-                b4["cc"].append(a4.take(C4, torch.uint8))
-                b4["cs"].append(a4.take(C4 // BLOCK, torch.float32))
-            b4["oc"], b4["os"] = a4.take(C4, torch.uint8), a4.take(C4 // BLOCK, torch.float32)
-            b4["out"] = a4.take(n4, torch.bfloat16)
+            b4 = fused_set(torch, dev, n4, N, torch.bfloat16)
+            b4["x"] = torch.empty(n4, dtype=torch.bfloat16, device=dev)
             if k == 0:
                 for r in range(N):
                     x4 = inputs.device_rank_buffer(inputs.LP_256MIB_BF16, r, dev)
@@ -548,8 +631,7 @@ def main():
                 for r in range(N):
                     lpc.lpc_reduce_scatter_chunk(b4["codes"], b4["scales"], r, b4["cc"][r], b4["cs"][r])
             else:
-                for key in ("x",):
-                    b4[key].copy_(sets4[0][key])
+                b4["x"].copy_(sets4[0]["x"])
                 for key in ("codes", "scales", "cc", "cs"):
                     for dst, src in zip(b4[key], sets4[0][key]):
                         dst.copy_(src)
@@ -565,15 +647,11 @@ def main():
             b = sets4[i % COPIES]
             lpc.lpc_quantize_fp8(b["x"], b["codes"][0], b["scales"][0])
 
-        for i in range(2 * COPIES):
-            fused4(i)
-            quantize4(i)
-        torch.cuda.synchronize()
-        kernels["rs_ag_fused_bf16_256MiB"] = stats(timer.run(fused4, 20), 20, fused_bytes(n4, N, 2))
-        kernels["quantize_bf16_256MiB"] = stats(timer.run(quantize4, 20), 20, quantize_bytes(n4, 2))
+        kernels["rs_ag_fused_bf16_256MiB"] = timer.measure(fused4, 3, 20, 2, fused_bytes(n4, N, 2))
+        kernels["quantize_bf16_256MiB"] = timer.measure(quantize4, 3, 20, 2, quantize_bytes(n4, 2))
         for b in sets4:
             assert torch.equal(b["oc"], sets4[0]["cc"][0]), "256 MiB bf16: reduced chunk differs"
-        del sets4, b4, a4
+        del sets4, b4
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
@@ -583,21 +661,10 @@ def main():
         sizes = {}
         for mib in (16, 32, 64, 128):
             ns = mib * 2 ** 20 // 4
-            Cs = ns // N
-            layout = [ns, ns // BLOCK * 4] * N + [Cs, Cs // BLOCK * 4] * (N + 1) + [ns * 4]
-            copies = max(2, -(-3 * MALL_BYTES // sum(layout)))
+            copies = max(2, -(-3 * MALL_BYTES // sum(fused_layout(ns, N, 4))))
             sets_s = []
             for k in range(copies):
-                a_s = Arena(torch, dev, layout)
-                b_s = dict(codes=[], scales=[], cc=[], cs=[])
-                for r in range(N):
-                    b_s["codes"].append(a_s.take(ns, torch.uint8))
-                    b_s["scales"].append(a_s.take(ns // BLOCK, torch.float32))
-                for r in range(N):
-                    b_s["cc"].append(a_s.take(Cs, torch.uint8))
-                    b_s["cs"].append(a_s.take(Cs // BLOCK, torch.float32))
-                b_s["oc"], b_s["os"] = a_s.take(Cs, torch.uint8), a_s.take(Cs // BLOCK, torch.float32)
-                b_s["out"] = a_s.take(ns, torch.float32)
+                b_s = fused_set(torch, dev, ns, N, f32)
                 if k == 0:
                     for r in range(N):
                         xs_r = inputs.device_rank_buffer(inputs.LP_16MIB, r, dev, n=ns)
@@ -617,16 +684,13 @@ def main():
                 lpc.lpc_rs_ag_fused(b["codes"], b["scales"], 0, b["oc"], b["os"], [None] + b["cc"][1:],
                                     [None] + b["cs"][1:], b["out"])
 
-            for i in range(2 * copies):
-                fused_s(i)
-            torch.cuda.synchronize()
-            d = stats(timer.run(fused_s, 40), 40, fused_bytes(ns, N, 4))
+            d = timer.measure(fused_s, 3, L, WB, fused_bytes(ns, N, 4))
             d["frac"] = round(d["gbps"] / HBM_PEAK_GBPS, 4)
             d["copies"] = copies
             sizes["%dMiB" % mib] = d
             for b in sets_s:
                 assert torch.equal(b["oc"], sets_s[0]["cc"][0]), "fused %d MiB: reduced chunk differs" % mib
-            del sets_s, b_s, a_s, fused_s
+            del sets_s, b_s, fused_s
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
         kernels["rs_ag_fused_f32_by_size"] = sizes
@@ -643,34 +707,34 @@ def main():
         for k in range(COPIES):
             a5 = Arena(torch, dev, [m5 * 2, m5, m5 // BLOCK * 4, m5 * 2])
             b5 = dict(x=a5.take(m5, torch.bfloat16).view(rows, row_len),
-                      codes=a5.take(m5, torch.uint8).view(rows, row_len),
-                      scales=a5.take(m5 // BLOCK, torch.float32).view(rows, row_len // BLOCK),
-                      back=a5.take(m5, torch.bfloat16).view(rows, row_len))
+                      codes=a5.take(m5, u8).view(rows, row_len),
+                      scales=a5.take(m5 // BLOCK, f32).view(rows, row_len // BLOCK),
+                      back=a5.take(m5, torch.bfloat16).view(rows, row_len), arena=a5)
             b5["x"].copy_(xr0)
             lpc.lpc_quantize_fp8_rows(b5["x"], perm, b5["codes"], b5["scales"])
             lpc.lpc_dequantize_fp8(b5["codes"], b5["scales"], b5["back"])
             sets5.append(b5)
         del xr0
         torch.cuda.synchronize()
-        kernels["a2av_route_16384"] = stats(timer.run(
-            lambda i: lpc.lpc_a2av_route(dest, N, counts, offsets, perm), 20), 20, rows * 4 * 2 + N * 8)
-        kernels["a2av_quantize_rows_bf16"] = stats(timer.run(
+        kernels["a2av_route_16384"] = timer.measure(
+            lambda i: lpc.lpc_a2av_route(dest, N, counts, offsets, perm), 3, 20, 2, rows * 4 * 2 + N * 8)
+        kernels["a2av_quantize_rows_bf16"] = timer.measure(
             lambda i: lpc.lpc_quantize_fp8_rows(sets5[i % COPIES]["x"], perm, sets5[i % COPIES]["codes"],
-                                                sets5[i % COPIES]["scales"]), 20), 20,
+                                                sets5[i % COPIES]["scales"]), 3, 20, 2,
             quantize_bytes(m5, 2) + rows * 4)
-        kernels["a2av_dequantize_bf16"] = stats(timer.run(
+        kernels["a2av_dequantize_bf16"] = timer.measure(
             lambda i: lpc.lpc_dequantize_fp8(sets5[i % COPIES]["codes"], sets5[i % COPIES]["scales"],
-                                             sets5[i % COPIES]["back"]), 20), 20, m5 + m5 // BLOCK * 4 + m5 * 2)
+                                             sets5[i % COPIES]["back"]), 3, 20, 2, m5 + m5 // BLOCK * 4 + m5 * 2)
         del sets5, b5, a5
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
     if args.copy_probe:
-        # a plain copy of known size (64 MiB read, 64 MiB written): the DDA-tree gather copy
-        src = [torch.ones(2 * 2 ** 20, dtype=torch.float32, device=dev) for _ in range(N)]
-        dst = torch.empty(16 * 2 ** 20, dtype=torch.float32, device=dev)
+        # a plain copy of known size (64 MiB read, 64 MiB written): the counter calibration
+        src = torch.ones(64 * 2 ** 20, dtype=u8, device=dev)
+        dst = torch.empty(64 * 2 ** 20, dtype=u8, device=dev)
         for _ in range(5):
-            lpc.dda_tree_allgather(src, dst)
+            lpc.lpc_measure_stream(src, 64 * 2 ** 20, dst, 64 * 2 ** 20)
         torch.cuda.synchronize()
 
     traffic = traffic_from_profiles("rs_ag_fused_kernel<8,float>")
@@ -694,7 +758,9 @@ def main():
             "nranks": N, "elems_per_rank": n, "block": BLOCK,
             "step": "quantize + fused RS+AG + DDA flat 64 KiB",
             "buffer_sets": S, "set_bytes": set_bytes, "hbm_resident": True,
-            "timing": "kernels: back-to-back batch behind a spin kernel, HIP events around it; step: HIP graph replay",
+            "timing": "kernels: %d batches of %d warm-up + %d launches back to back behind a spin kernel, "
+                      "each batch after a read-only pass over 1 GiB, HIP events on the launch stream; "
+                      "step: K steps back to back behind a spin kernel, HIP events" % (B, WB, L),
         },
         "roofline": {
             "bound": "hbm",
@@ -705,13 +771,26 @@ def main():
             "traffic": traffic,
             "kernel": "rs_ag_fused_kernel<8,float>",
             "bytes_per_launch": fb,
-            "mean_us": round(f_us, 3),
-            "launches": kernels["rs_ag_fused_f32_16MiB"]["launches"],
-            # context: an empty launch's share of mean_us on this GPU, and the rate of the rest
-            "empty_launch_us": round(floor_us, 3),
-            "beyond_empty_launch_gbps": round(fb / max(f_us - floor_us, 1e-3) / 1e3, 1),
+            "read_bytes_per_launch": fr,
+            "write_bytes_per_launch": fw,
+            "mean_us": hk["us"],
+            "median_us": hk["median_us"],
+            "min_us": hk["min_us"],
+            "max_us": hk["max_us"],
+            "launches": B * L,
+            # the same run's references: a plain kernel with the same bytes and read:write mix, an empty
+            # launch of the fused kernel's shape, and a minimal empty launch
+            "ceiling_kernel": "lpc_measure_stream, %d B read + %d B written" % (fr, fw),
+            "ceiling_us": ceil_f["us"],
+            "ceiling_gbps": ceil_f["gbps"],
+            "frac_of_ceiling": hk["frac_of_ceiling"],
+            "floor_us": floor_f["us"],
+            "floor_shape": hk["floor_shape"],
+            "empty_launch_us": empty["us"],
+            "in_step_us": hk["in_step_us"],
         },
         "kernels": kernels,
+        "step_parts": step_parts,
         "dda_flat_n8_bf16": dda_res,
         "dda_flat_us_64KiB": dda_res["64KiB"]["us"],
         "step_wall_s": round(wall_s, 6),

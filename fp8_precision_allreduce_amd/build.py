@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblpc.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("lpc_kernels.hip", "lpc_api.hip", "lpc_allreduce.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("lpc_kernels.hip", "lpc_api.hip", "lpc_allreduce.hip",
+                                           "lpc_measure.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -30,13 +31,29 @@ FLAGS = [
 ]
 
 
+# The packed-FP32 switch is a device-code-generator feature: hipcc hands it to
+# the host compilation too, whose target does not know it and says so once per
+# source.  That one message is dropped; everything else the compiler prints is
+# passed on.
+_HOST_FEATURE_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
+
+
+def _run(cmd) -> None:
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if l.strip() != _HOST_FEATURE_NOTE)
+    if out.strip():
+        print(out, file=sys.stderr, flush=True)
+    if p.returncode != 0:
+        raise subprocess.CalledProcessError(p.returncode, cmd)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into liblpc.so (always recompiles); returns its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    _run(cmd)
     os.replace(tmp, LIB)
     return LIB
 
@@ -47,8 +64,7 @@ def assembly(out_dir: str) -> list:
     outs = []
     for src in SOURCES:
         out = os.path.join(out_dir, os.path.basename(src) + ".s")
-        subprocess.check_call([HIPCC, *[f for f in FLAGS if f not in ("-shared",)], "-S",
-                               "--cuda-device-only", "-o", out, src])
+        _run([HIPCC, *[f for f in FLAGS if f not in ("-shared",)], "-S", "--cuda-device-only", "-o", out, src])
         outs.append(out)
     return outs
 

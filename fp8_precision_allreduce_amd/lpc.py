@@ -21,6 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblpc.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "lpc.h")
+MEASURE_HEADER = os.path.join(os.path.dirname(_HERE), "include", "lpc_measure.h")
 
 BLOCK = 128
 MAX_RANKS = 8
@@ -60,6 +61,9 @@ SIGNATURES = {
     "lpc_allreduce_workspace_bytes": [_int, _int, _sz, _int, ctypes.POINTER(ctypes.c_size_t)],
     "lpc_allreduce_emulated": [_pp, _int, _sz, _int, _int, _vp, _sz, _vp],
     "lpc_allreduce_emulated_noalloc": [_pp, _int, _sz, _int, _int, _vp],
+    # reference kernels for measurement (include/lpc_measure.h)
+    "lpc_measure_stream": [_vp, _sz, _vp, _sz, _vp],
+    "lpc_measure_empty": [ctypes.c_uint, ctypes.c_uint, ctypes.c_uint, _sz, _vp, _vp],
 }
 
 _lock = threading.Lock()
@@ -89,9 +93,9 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def header_functions() -> list:
-    """Names of the functions include/lpc.h declares."""
-    text = open(HEADER).read()
+def header_functions(header: str = HEADER) -> list:
+    """Names of the functions a header under include/ declares (lpc.h by default)."""
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -278,6 +282,22 @@ def lpc_allreduce_emulated_noalloc(bufs, algo: int, stream=None):
     n = bufs[0].numel()
     dt = bufs[0].dtype
     _call("lpc_allreduce_emulated_noalloc", _ptrs(bufs, "bufs", (dt,), n), N, n, _dtype(bufs[0]), algo,
+          _stream(stream))
+
+
+def lpc_measure_stream(src, read_bytes: int, dst, write_bytes: int, stream=None):
+    """Plain streaming kernel (measurement reference): reads read_bytes of src, writes write_bytes of dst."""
+    if src is not None and src.numel() * src.element_size() < read_bytes:
+        raise ValueError("src holds fewer than %d bytes" % read_bytes)
+    if dst is not None and dst.numel() * dst.element_size() < write_bytes:
+        raise ValueError("dst holds fewer than %d bytes" % write_bytes)
+    _call("lpc_measure_stream", _dev(src, "src") if src is not None else None, read_bytes,
+          _dev(dst, "dst") if dst is not None else None, write_bytes, _stream(stream))
+
+
+def lpc_measure_empty(grid_x: int, grid_y: int, threads: int, kernarg_bytes: int, sink, stream=None):
+    """Empty launch of the given shape (measurement reference); sink is never written."""
+    _call("lpc_measure_empty", grid_x, grid_y, threads, kernarg_bytes, _dev(sink, "sink", None, 1),
           _stream(stream))
 
 

@@ -45,11 +45,38 @@ def test_header_limits_match_binding():
 
 
 def test_exports_every_declared_function(L):
-    names = lpc.header_functions()
-    assert len(names) >= 14
+    import glob
+    import os
+
+    headers = sorted(glob.glob(os.path.join(os.path.dirname(lpc.HEADER), "*.h")))
+    assert lpc.HEADER in headers and lpc.MEASURE_HEADER in headers
+    names = set()
+    for h in headers:
+        names |= set(lpc.header_functions(h))
+    assert len(names) >= 18
     for name in names:
         assert hasattr(L, name), name
-    assert set(lpc.SIGNATURES) | {"lpc_status_string", "lpc_abi_version"} == set(names)
+    assert set(lpc.SIGNATURES) | {"lpc_status_string", "lpc_abi_version"} == names
+
+
+def test_measure_errors(L):
+    s, e = L.lpc_measure_stream, L.lpc_measure_empty
+    assert s(A, 16, A, 16 * 3 + 8, None) == SHAPE
+    assert s(A, 20, A, 16, None) == SHAPE
+    assert s(None, 0, None, 0, None) == OK
+    assert s(None, 16, A, 16, None) == NULL
+    assert s(A, 16, None, 16, None) == NULL
+    assert s(B, 16, A, 16, None) == ALIGN
+    assert s(A, 16, B, 16, None) == ALIGN
+    assert s(A, 16, A + 1024, 32, None) == HIP            # passes the checks; no device
+    assert e(0, 1, 64, 8, A, None) == SHAPE
+    assert e(1, 0, 64, 8, A, None) == SHAPE
+    assert e(1, 1, 0, 8, A, None) == SHAPE
+    assert e(1, 1, 2048, 8, A, None) == SHAPE
+    assert e(1, 1, 64, 513, A, None) == SHAPE
+    assert e(1, 1, 64, 8, None, None) == NULL
+    assert e(1, 1, 64, 8, B, None) == ALIGN
+    assert e(4, 2, 256, 300, A, None) == HIP
 
 
 def test_abi_version_matches_header(L):
