@@ -45,7 +45,11 @@
  *     (LPC_ERR_RANKS), n == 0 (returns LPC_OK, no work), null pointers
  *     (LPC_ERR_NULL), 16-byte alignment of every pointer (LPC_ERR_ALIGN),
  *     shape (LPC_ERR_SHAPE).  A failed kernel launch gives LPC_ERR_HIP.
- *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.  The
+ *     FP32 rank-order sum of every element must be finite as well (for
+ *     example |x| <= FLT_MAX / nranks everywhere): a block whose sum
+ *     overflows has an infinite absmax, and its requantized codes and scale
+ *     are unspecified.
  *   - Outputs must not overlap inputs unless a call says otherwise.
  *   - No call throws; every call is extern "C".
  */
@@ -118,7 +122,12 @@ lpc_status lpc_reduce_scatter_chunk(const uint8_t *const codes[], const float *c
 /* (3) All-gather dequantization: out[p*C + i] = fl32(E4M3(chunk_codes[p][i])
  * * chunk_scales[p][i/128]), rounded to bf16 (nearest-even) when out_t is
  * LPC_BF16.  The owner's chunk is also taken from its requantized form, so
- * every rank ends with the same values.
+ * every rank ends with the same values.  This is the all-gather phase of the
+ * two-phase allreduce (infolabhq pages, "Direct Data Access (DDA)" section,
+ * DDA tree: reduce-scatter, then all-gather) carried out on the data of the
+ * second quantization of a low-precision AllReduce (RCCLX post, es copy,
+ * "Colectivos de mengua precisión": FP8 on the wire, FP32 compute, one or two
+ * quantizations per collective).
  *   chunk_codes[p] [C], chunk_scales[p] [C/128]: rank p's requantized chunk
  *   n    elements of the output (= nranks*C); multiple of 128*nranks
  *   out  [n] of type out_t.  `out` may be the caller's original input buffer
@@ -132,7 +141,11 @@ lpc_status lpc_allgather_dequant(const uint8_t *const chunk_codes[], const float
  * from registers into out[rank*C ..], and the dequantization of the other
  * ranks' requantized chunks into the rest of `out`.  Results are
  * byte-identical to lpc_reduce_scatter_chunk followed by
- * lpc_allgather_dequant.
+ * lpc_allgather_dequant.  The operation is the low-precision AllReduce's two
+ * phases after the first quantization, reduce-scatter with FP32 compute and
+ * the second quantization, then all-gather (RCCLX post, es copy, "Colectivos
+ * de mengua precisión"; the two phases as in infolabhq's "Direct Data Access
+ * (DDA)" section, DDA tree).
  *   codes[], scales[]    as for lpc_reduce_scatter_chunk
  *   peer_chunk_codes[p], peer_chunk_scales[p]  rank p's requantized chunk
  *                        for p != rank ([rank] is ignored and may be NULL)
@@ -175,12 +188,17 @@ lpc_status dda_flat_reduce(const void *const bufs[], int nranks, size_t n, void 
                            hipStream_t stream);
 
 /* DDA tree, reduce-scatter phase, unquantized: out[i] = sum over p in rank
- * order of bufs[p][rank*C + i], FP32 accumulation, written in `t`.
+ * order of bufs[p][rank*C + i], FP32 accumulation, written in `t`
+ * (infolabhq pages, "Direct Data Access (DDA)" section, DDA tree: the
+ * allreduce split into reduce-scatter and all-gather, each phase reading the
+ * peers' memory directly).
  *   bufs[p] [n] of type t;  out [C] of type t;  n multiple of 8*nranks.     */
 lpc_status dda_tree_reduce_scatter(const void *const bufs[], lpc_dtype t, int nranks, int rank,
                                    size_t n, void *out, hipStream_t stream);
 
-/* DDA tree, all-gather phase: out[p*C + i] = chunks[p][i] (a gather copy).
+/* DDA tree, all-gather phase: out[p*C + i] = chunks[p][i] (a gather copy)
+ * (infolabhq pages, "Direct Data Access (DDA)" section, DDA tree: the second
+ * phase, every rank reading the peers' reduced chunks directly).
  *   chunks[p] [C] of type t;  out [n] of type t;  n multiple of 8*nranks.   */
 lpc_status dda_tree_allgather(const void *const chunks[], lpc_dtype t, int nranks, size_t n,
                               void *out, hipStream_t stream);
@@ -204,7 +222,11 @@ lpc_status lpc_a2av_route(const int32_t *dest, size_t rows, int nranks,
 
 /* Gather-and-quantize rows into the packed send buffer: packed row j is the
  * blockwise quantization of source row perm[j] of x (rows x row_len, row
- * major).  A perm entry outside [0, rows) gives an all-zero packed row
+ * major).  This is the one quantization of a low-precision AlltoAll (RCCLX
+ * post, es copy, "Colectivos de mengua precisión": AlltoAll among the LP
+ * collectives, FP8 on the wire), applied to the variable per-destination
+ * row counts of AllToAllvDynamic (same post, introduction: CTran's
+ * GPU-resident AllToAllvDynamic collective).  A perm entry outside [0, rows) gives an all-zero packed row
  * (codes 0, scales +0).
  *   codes [rows x row_len], scales [rows x row_len/128], packed order
  *   row_len multiple of 128 (else LPC_ERR_SHAPE).                             */
@@ -214,6 +236,8 @@ lpc_status lpc_quantize_fp8_rows(const void *x, lpc_dtype in, size_t rows, size_
 
 /* Dequantize a flat quantized buffer (e.g. received all-to-all rows):
  * out[i] = fl32(E4M3(codes[i]) * scales[i/128]) as float, or bf16 rounded.
+ * The receive side of a low-precision AlltoAll: FP8 data back to FP32/BF16
+ * for compute (RCCLX post, es copy, "Colectivos de mengua precisión").
  *   n multiple of 128.                                                        */
 lpc_status lpc_dequantize_fp8(const uint8_t *codes, const float *scales, size_t n,
                               void *out, lpc_dtype out_t, hipStream_t stream);
@@ -318,7 +342,10 @@ lpc_status lpc_allreduce_emulated_noalloc(void *const bufs[], int nranks, size_t
 
 /* Raw codec: codes[i] = E4M3 of the already-scaled value x[i], nearest-even,
  * saturating at +-448, sign kept (the conversion every quantizing kernel
- * applies to fl32(x / s)).  n: any count.                                    */
+ * applies to fl32(x / s)).  It is the FP8 encoding of the low-precision
+ * collectives (RCCLX post, es copy, "Colectivos de mengua precisión", where
+ * the range of FP8 decides what is representable); the pages name no FP8
+ * variant, and this library reads it as OCP E4M3FN.  n: any count.          */
 lpc_status lpc_e4m3_encode(const float *x, size_t n, uint8_t *codes, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */

@@ -735,7 +735,8 @@ def test_a2av_quantize_rows_small(dev, orc):
                 rs[k] = 0.0
         assert_same(to_host(codes), rc, "rows codes")
         assert_same(to_host(scales), rs, "rows scales")
-    # rows longer than 1024 granules take the multi-workgroup path
+    # long rows (16,640 elements, 130 blocks): a row spans many workgroups' granule tiles, and tiles
+    # start and end inside rows
     x2 = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.A2AV, 1), 6 * 128 * 130, 1.0)).reshape(6, -1)
     p2 = np.array([5, 0, 3, 1, 4, 2], np.int32)
     say("a2av quantize long rows", x2.shape)
@@ -889,9 +890,10 @@ def test_comm_pages_quickstart(dev, N):
             assert torch.all(t.float() == expect), (dt, algo, t.float().unique())
 
 
-def test_a2av_quantize_rows_more_than_grid_y(dev, orc):
-    """70,000 short rows: more rows than one launch's grid.y (65,535), so workgroups loop
-    over rows; perm from the router, checked in full against the oracle."""
+def test_a2av_quantize_rows_70000_short_rows(dev, orc):
+    """70,000 short rows (one block each): more rows than the 65,535 a grid dimension can count,
+    which the flat granule kernel handles as a single 1-D range; perm from the router (with
+    512-lane workgroups past 18,432 rows), checked in full against the oracle."""
     rows, row_len = 70_000, 128
     x = inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.A2AV, 2), rows * row_len, 1.0)).reshape(rows, row_len)
     dest = inputs.zipf_destinations(rows=rows)
