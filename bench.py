@@ -24,10 +24,10 @@ Timing.  Every figure comes from HIP events on the stream the kernels run on.
     untimed launches, then --launches launches back to back between two
     events.  mean_us = mean over all measured launches; median_us, min_us and
     max_us are over the batch means.
-  * ms_per_step: the K steps launched back to back behind a spin kernel,
-    between two events (synchronized before and after).  The same timing
-    with one kernel left out of every step gives each kernel's marginal cost
-    inside the step (step_parts).
+  * ms_per_step: --warmup untimed steps, then the K steps back to back
+    between two events, all behind one spin kernel (synchronized before and
+    after).  The same timing with one kernel left out of every step gives
+    each kernel's marginal cost inside the step (step_parts).
 The timed launches cycle through enough buffer copies (--sets) that the
 Infinity Cache cannot hold them, so the kernels stream from HBM.
 
@@ -272,28 +272,6 @@ class BatchTimer:
             d["gbps"] = round(nbytes / d["us"] / 1e3, 1)
         return d
 
-    def sequence(self, fn, count: int) -> float:
-        """fn(0 .. count-1) back to back behind one spin, between two events (synchronized
-        before and after); mean device microseconds per call."""
-        torch = self.torch
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(min(count, 4)):
-            fn(i)
-        host_us = (time.perf_counter() - t0) * 1e6 / min(count, 4)
-        torch.cuda.synchronize()
-        if self.evict is not None:
-            self.evict()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(self.cycles_per_us * (host_us * count * 2.0 + 1000.0)))
-        e0.record()
-        for i in range(count):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / count
-
 
 class Arena:
     """The buffers of one set carved, in order, from a single allocation (4 KiB
@@ -477,21 +455,21 @@ def main():
         if "d" in parts:
             dda(4, i)
 
-    # -- warmup, then the timed region: exactly K steps ---------------------------------------------
+    # -- the timed region: W untimed warm-up steps, then exactly K steps between two events --------
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    K = args.steps
+    K, W = args.steps, args.warmup
     timer = BatchTimer(torch, evict)
     log("timing %d steps" % K)
     t_wall = time.perf_counter()
-    step_us = timer.sequence(step, K)
+    step_us, step_fed = timer.batch(step, 0, W, K)
     wall_s = time.perf_counter() - t_wall
     total_ms = step_us * K / 1e3
-    # each kernel's marginal cost inside the step: the same K steps with that kernel left out
-    step_parts = {"step_us": round(step_us, 3)}
+    # each kernel's marginal cost inside the step: the same steps with that kernel left out
+    step_parts = {"step_us": round(step_us, 3), "gpu_fed": bool(step_fed)}
     for part, name in (("fd", "quantize"), ("qd", "rs_ag_fused"), ("qf", "dda_flat")):
-        t = timer.sequence(lambda i, part=part: step(i, part), K)
+        t, _ = timer.batch(lambda i, part=part: step(i, part), 0, W, K)
         step_parts["without_%s_us" % name] = round(t, 3)
         step_parts["%s_in_step_us" % name] = round(step_us - t, 3)
 
@@ -760,7 +738,7 @@ def main():
             "buffer_sets": S, "set_bytes": set_bytes, "hbm_resident": True,
             "timing": "kernels: %d batches of %d warm-up + %d launches back to back behind a spin kernel, "
                       "each batch after a read-only pass over 1 GiB, HIP events on the launch stream; "
-                      "step: K steps back to back behind a spin kernel, HIP events" % (B, WB, L),
+                      "step: W warm-up + K steps back to back behind a spin kernel, HIP events" % (B, WB, L),
         },
         "roofline": {
             "bound": "hbm",
