@@ -359,6 +359,42 @@ def pin_identical_buffers(o):
             assert np.array_equal(res["out"], (deq * N).astype(np.float32))
 
 
+def _ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in units in the last place between same-signed finite float32 arrays."""
+    return np.abs(bits(a).astype(np.int64) - bits(b).astype(np.int64))
+
+
+def pin_identical_buffers_n8(o):
+    """N = 8 identical buffers (survey P6): every rank-order FP32 sum lies within 2 ulp of
+    8 d, the requantized codes equal the original codes, and every new scale lies within
+    3 ulp of 8 s.  8 d is exact (a power-of-two multiple).  The sum's bound: d + d is
+    exact, and each of the six later additions errs by at most half an ulp of its result,
+    which is at most half an ulp of 8 d (a quarter for the two results below 4 d): at most
+    2.5 ulp of 8 d in all, so at most 2 whole ulps.  The scale's: the block absmax of the
+    sums is within 2 ulp of 8 fl32(448 s), and fl32(448 s) and the division by 448 round once
+    each.  Both bounds are reached: 2 and 3 ulp over 8,192 blocks with 0.1% of the values
+    scaled by 100."""
+    g = np.random.Generator(np.random.PCG64(31))
+    N = 8
+    x = inputs.normal_f32(g, N * BLOCK * 1024, 1.0)
+    x[::997] *= np.float32(100.0)
+    codes, scales = o.quantize(x)
+    d = (torch_e4m3_table()[codes].reshape(-1, BLOCK) * scales[:, None]).reshape(-1).astype(np.float32)
+    res = o.lp_allreduce([x] * N)
+    C = x.size // N
+    for r in range(N):
+        sl, sb = slice(r * C, (r + 1) * C), slice(r * C // BLOCK, (r + 1) * C // BLOCK)
+        eight_d = d[sl] * np.float32(8.0)
+        assert np.array_equal(eight_d.astype(np.float64), d[sl].astype(np.float64) * 8)
+        acc = o.reduce_scatter_out([codes] * N, [scales] * N, r)
+        nz = eight_d != 0
+        assert np.all(acc[~nz] == 0)
+        assert _ulps(acc[nz], eight_d[nz]).max() <= 2, "sum of 8 identical values off by more than 2 ulp"
+        assert np.array_equal(res["chunk_codes"][r], codes[sl]), "requantized codes changed"
+        s8 = scales[sb] * np.float32(8.0)
+        assert _ulps(res["chunk_scales"][r], s8).max() <= 3, "new scale off by more than 3 ulp"
+
+
 def pin_pages_example(o):
     """The pages' quick-start: 10x20 tensors filled with the rank, all-reduced with SUM,
     give N(N-1)/2 everywhere (golden values with their citation in tests/golden)."""
