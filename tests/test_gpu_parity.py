@@ -543,10 +543,13 @@ def test_lp_allreduce_n8_16MiB_full(dev, orc):
     compare_allreduce(res, orc.lp_allreduce(xs), "n8 16MiB")
 
 
-def test_lp_allreduce_n8_256MiB_bf16_sampled(dev, orc):
+def test_lp_allreduce_n8_256MiB_bf16(dev, orc):
     """The 256 MiB bf16 workload at full size (N=8, 256 MiB bf16 per rank, Laplace): the whole path
-    on the GPU (fused kernel for ranks 0 and 7), checked on 96 sampled blocks per
-    chunk: every rank's codes and scales there, the reduced chunk, and the output."""
+    on the GPU (fused kernel for ranks 0 and 7).  The last chunk (rank 7's, at the highest
+    offsets of every buffer: 16,777,216 elements) is compared in full: every rank's codes and
+    scales over it, the requantized chunk, and both fused launches' bf16 output over it (rank
+    7's from registers, rank 0's from the peer chunk).  The other chunks are compared on 96
+    sampled blocks each, first and last block included."""
     N = 8
     n = inputs.WORKLOADS[inputs.LP_256MIB_BF16]["n"]
     C = n // N
@@ -560,6 +563,7 @@ def test_lp_allreduce_n8_256MiB_bf16_sampled(dev, orc):
     for r in range(N):
         lpc.lpc_reduce_scatter_chunk(codes, scales, r, cc[r], cs[r])
     g = np.random.Generator(np.random.PCG64(107))
+    outs = []
     for r in (0, N - 1):
         out = torch.empty(n, dtype=torch.bfloat16, device=dev)
         own_c = torch.empty(C, dtype=torch.uint8, device=dev)
@@ -590,8 +594,28 @@ def test_lp_allreduce_n8_256MiB_bf16_sampled(dev, orc):
             assert_same(to_host(cs[p][torch.from_numpy(blocks).to(dev)]), sum_scales, "256 MiB chunk scales %d" % p)
             ref_out = orc.dequantize(sum_codes, sum_scales, bf16=True)
             assert_same(to_host(out[idx]), ref_out, "256 MiB out rank %d chunk %d" % (r, p))
-        del out
-    del xs, codes, scales, cc, cs
+        outs.append(out)
+    # the last chunk in full: the oracle over that chunk of every rank's buffer
+    p = N - 1
+    sl, slb = slice(p * C, (p + 1) * C), slice(p * C // BLOCK, (p + 1) * C // BLOCK)
+    say("lp allreduce 256 MiB bf16: chunk %d in full (%d elements per rank)" % (p, C))
+    qc = []
+    for s_ in range(N):
+        rc, rs = orc.quantize(to_host(xs[s_][sl]), bf16=True)
+        assert_same(to_host(codes[s_][sl]), rc, "256 MiB chunk %d codes rank %d (full)" % (p, s_))
+        assert_same(to_host(scales[s_][slb]), rs, "256 MiB chunk %d scales rank %d (full)" % (p, s_))
+        full_c = np.zeros(n, np.uint8)
+        full_s = np.zeros(n // BLOCK, np.float32)
+        full_c[sl], full_s[slb] = rc, rs
+        qc.append((full_c, full_s))
+    sum_codes, sum_scales = orc.reduce_scatter_chunk([c for c, _ in qc], [s_ for _, s_ in qc], p)
+    del qc
+    assert_same(to_host(cc[p]), sum_codes, "256 MiB chunk %d requantized codes (full)" % p)
+    assert_same(to_host(cs[p]), sum_scales, "256 MiB chunk %d requantized scales (full)" % p)
+    ref_out = orc.dequantize(sum_codes, sum_scales, bf16=True)
+    for r, out in zip((0, N - 1), outs):
+        assert_same(to_host(out[sl]), ref_out, "256 MiB out rank %d chunk %d (full)" % (r, p))
+    del xs, codes, scales, cc, cs, outs
     torch.cuda.empty_cache()
 
 
@@ -748,9 +772,10 @@ def test_a2av_quantize_rows_small(dev, orc):
     assert_same(to_host(scales), rs, "long rows scales")
 
 
-def test_a2av_16384x7168_sampled(dev, orc):
+def test_a2av_16384x7168(dev, orc):
     """The all-to-all-v workload at full size: route, quantize + pack all 16,384 x 7168 rows, dequantize
-    the packed buffer; 192 packed rows checked against the oracle."""
+    the packed buffer; the permutation, every packed row's codes and scales and the whole
+    dequantized buffer compared with the oracle."""
     rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
     say("a2av full rows=%d row_len=%d" % (rows, row_len))
     x = inputs.a2av_rows()
@@ -768,14 +793,15 @@ def test_a2av_16384x7168_sampled(dev, orc):
     torch.cuda.synchronize()
     rc, ro, rp = orc.a2av_route(dest, 8)
     assert_same(to_host(perm), rp, "a2av perm")
+    assert_same(to_host(counts), rc, "a2av counts")
+    assert_same(to_host(offsets), ro, "a2av offsets")
     assert int(to_host(counts).sum()) == rows
-    g = np.random.Generator(np.random.PCG64(109))
-    ks = np.concatenate([[0, rows - 1], ro, g.choice(rows, 180, replace=False)]).astype(np.int64)
-    for k in ks:
-        c, s = orc.quantize(x[rp[k]], bf16=True)
-        assert_same(to_host(codes[k]), c, "a2av packed row %d codes" % k)
-        assert_same(to_host(scales[k]), s, "a2av packed row %d scales" % k)
-        assert_same(to_host(back[k]), orc.dequantize(c, s, bf16=True), "a2av dequant row %d" % k)
+    say("a2av full: oracle quantize + dequantize of all %d rows" % rows)
+    qc, qs = orc.quantize_rows(x, rp, bf16=True)
+    assert_same(to_host(codes), qc.reshape(rows, row_len), "a2av packed codes (all rows)")
+    assert_same(to_host(scales), qs.reshape(rows, row_len // BLOCK), "a2av packed scales (all rows)")
+    ref_back = orc.dequantize(qc.reshape(-1), qs.reshape(-1), bf16=True)
+    assert_same(to_host(back).reshape(-1), ref_back, "a2av dequantized rows (all)")
 
 
 # -- emulated allreduce (size-based dispatch, torchcomms-shaped wrapper) ------------------------------
