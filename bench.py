@@ -28,8 +28,12 @@ Timing.  Every figure comes from HIP events on the stream the kernels run on.
     between two events, all behind one spin kernel (synchronized before and
     after).  The same timing with one kernel left out of every step gives
     each kernel's marginal cost inside the step (step_parts).
-The timed launches cycle through enough buffer copies (--sets) that the
-Infinity Cache cannot hold them, so the kernels stream from HBM.
+Cold HBM.  Loads allocate their lines in the 256 MB Infinity Cache (the
+non-temporal stores of the outputs do not), so a launch whose inputs were
+read again too recently is partly served from it.  Every timed launch
+therefore cycles through enough buffer copies that at least 1 GiB (four
+times the cache) is read between two reads of the same copy: measured, the
+fused launch's time stopped changing once about 0.5 GB was read in between.
 
 value = algorithmic bytes of one fused RS+AG launch / its mean duration
 (GB/s).  The roofline object compares it with the 8 TB/s HBM peak and with
@@ -69,11 +73,14 @@ HBM_PEAK_GBPS = 8000.0
 BLOCK = 128
 NRANKS = 8
 MALL_BYTES = 256 * 2 ** 20
+COLD_READ_BYTES = 4 * MALL_BYTES          # bytes read between two reads of the same buffer copy
+ROUND_WAVES = 8192                        # wavefronts an MI355X holds at once at 8 per SIMD
 EVICT_BYTES = 2 ** 30
 THREADS = 256
 # kernel-argument bytes of the fused kernel: two RankCodes (8 code and 8 scale
-# pointers each), rank, C, and the chunk-code, chunk-scale and output pointers
-FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 3 * 8
+# pointers each), rank, C, the lane stride H, and the chunk-code, chunk-scale and
+# output pointers
+FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 8 + 3 * 8
 QUANT_KERNARG = 4 * 8                       # x, granule count, codes, scales
 
 
@@ -111,6 +118,22 @@ def quantize_bytes(n: int, in_size: int) -> int:
 
 def dda_bytes(n: int, N: int) -> int:
     return (N + 1) * n * 2
+
+
+def cold_copies(read_bytes: int) -> int:
+    """Buffer copies to cycle so that COLD_READ_BYTES are read between two reads of one copy."""
+    return max(2, -(-COLD_READ_BYTES // read_bytes) + 1)
+
+
+def fused_grid(n: int, N: int, out_size: int):
+    """(grid_x, grid_y) of the fused launch, as the library picks it: one slice per peer, one
+    lane vector per lane, or two (half a chunk apart) for fp32 output when one per lane would
+    take more than one round of wavefronts and the chunk is a multiple of 256 elements."""
+    C = n // N
+    lanes = C // (16 // out_size)
+    slices = max(1, N - 1)
+    v = 2 if (out_size == 4 and C % 256 == 0 and -(-lanes // THREADS) * slices * 4 > ROUND_WAVES) else 1
+    return -(-(lanes // v) // THREADS), slices
 
 
 KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every path kernel's device code lives in these two
@@ -329,7 +352,8 @@ def main():
     ap.add_argument("--batches", type=int, default=5, help="timed batches per kernel")
     ap.add_argument("--launches", type=int, default=100, help="timed launches per batch (the pages' 100)")
     ap.add_argument("--batch-warmup", type=int, default=10, help="untimed launches before each batch (the pages' 10)")
-    ap.add_argument("--sets", type=int, default=16, help="buffer copies of the 16 MiB workload cycled through")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="buffer copies of the 16 MiB workload cycled through (0: enough for cold HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true",
@@ -376,7 +400,9 @@ def main():
     torch.cuda.synchronize()
 
     # fused-launch sets (only what the fused launch touches) and quantize sets, each cycled
-    S = max(1, args.sets)
+    # every kernel that uses the fused sets reads at least one chunk of every rank (N x 528 KiB)
+    S = args.sets if args.sets > 0 else cold_copies(N * chunk_bytes(C))
+    SQ = args.sets if args.sets > 0 else cold_copies(n * 4)
     sets = []
     for _ in range(S):
         b = fused_set(torch, dev, n, N, f32)
@@ -388,7 +414,7 @@ def main():
         b["rs_out"] = torch.empty(C, dtype=f32, device=dev)
         sets.append(b)
     qsets = []
-    for _ in range(S):
+    for _ in range(SQ):
         a = Arena(torch, dev, [n * 4, n, n // BLOCK * 4])
         q = dict(x=a.take(n, f32), codes=a.take(n, u8), scales=a.take(n // BLOCK, f32), arena=a)
         q["x"].copy_(xs[0])
@@ -400,7 +426,7 @@ def main():
 
     def dda_sets(T):
         m = dda_host[T][0].size
-        count = max(64, -(-2 * MALL_BYTES // dda_bytes(m, N)))
+        count = cold_copies(N * m * 2)
         pool = torch.empty((count, N + 1, m), dtype=torch.bfloat16, device=dev)
         src = torch.stack([torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[T]])
         pool[:, :N].copy_(src.unsqueeze(0).expand(count, N, m))
@@ -417,7 +443,7 @@ def main():
 
     # -- the kernels --------------------------------------------------------------------------
     def quantize(i):
-        q = qsets[i % S]
+        q = qsets[i % SQ]
         lpc.lpc_quantize_fp8(q["x"], q["codes"], q["scales"])
 
     def fused_at(rank):
@@ -485,24 +511,25 @@ def main():
     }
     hk = kernels["rs_ag_fused_f32_16MiB"]
     # the same launch at the last rank (its chunk at the end of every buffer, its peers 0..6)
-    hk["rank%d_us" % (N - 1)] = timer.measure(fused_at(N - 1), 2, L, WB)["us"]
+    R7_BATCHES = 2
+    hk["rank%d_us" % (N - 1)] = timer.measure(fused_at(N - 1), R7_BATCHES, L, WB)["us"]
     hk["in_step_us"] = step_parts["rs_ag_fused_in_step_us"]
 
     # references in the same run: plain streaming kernels at the fused and quantize mixes, an
     # empty launch of each kernel's shape, and a minimal empty launch
-    pool_src = [torch.ones(32 * 2 ** 20, dtype=u8, device=dev) for _ in range(S)]
-    pool_dst = [torch.empty(32 * 2 ** 20, dtype=u8, device=dev) for _ in range(S)]
+    fr, fw = fused_read_bytes(n, N), fused_write_bytes(n, N, 4)
+    qr, qw = n * 4, n + n // BLOCK * 4
+    SP = cold_copies(min(fr, qr))
+    pool_src = [torch.ones(max(fr, qr), dtype=u8, device=dev) for _ in range(SP)]
+    pool_dst = [torch.empty(max(fw, qw), dtype=u8, device=dev) for _ in range(SP)]
 
     def stream(rb, wb):
         def f(i):
-            lpc.lpc_measure_stream(pool_src[i % S], rb, pool_dst[i % S], wb)
+            lpc.lpc_measure_stream(pool_src[i % SP], rb, pool_dst[i % SP], wb)
         return f
-
-    fr, fw = fused_read_bytes(n, N), fused_write_bytes(n, N, 4)
-    qr, qw = n * 4, n + n // BLOCK * 4
     ceil_f = timer.measure(stream(fr, fw), B, L, WB, fr + fw)
     ceil_q = timer.measure(stream(qr, qw), B, L, WB, qr + qw)
-    fgrid = (-(-C // (4 * THREADS)), N - 1)
+    fgrid = fused_grid(n, N, 4)
     qgrid = (-(-n // (16 * THREADS)), 1)
     floor_f = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_KERNARG, sink),
                             B, L, WB)
@@ -531,10 +558,13 @@ def main():
     dda_res["64KiB"]["in_step_us"] = step_parts["dda_flat_in_step_us"]
 
     # -- every launch left the eager result in place (the last launches on the fused sets were the
-    # rank N-1 ones, so each set holds rank N-1's requantized chunk) ------------------------------------
-    for b in sets:
-        assert torch.equal(b["oc"], cc[N - 1]), "reduced chunk differs from the eager result"
-        assert torch.equal(b["os"].view(torch.int32), cs[N - 1].view(torch.int32)), "chunk scales differ"
+    # rank N-1 ones, on sets 0 .. R7_LAUNCHES-1 mod S, so those hold rank N-1's requantized chunk and
+    # the others rank 0's) ----------------------------------------------------------------------------
+    r7_sets = {i % S for i in range(R7_BATCHES * (WB + L))}
+    for k, b in enumerate(sets):
+        r = N - 1 if k in r7_sets else 0
+        assert torch.equal(b["oc"], cc[r]), "reduced chunk differs from the eager result"
+        assert torch.equal(b["os"].view(torch.int32), cs[r].view(torch.int32)), "chunk scales differ"
         assert torch.equal(b["out"].view(torch.int32), out_ref.view(torch.int32)), "output differs"
     for q in qsets:
         assert torch.equal(q["codes"], codes[0]), "quantized buffer differs"
@@ -549,18 +579,20 @@ def main():
 
     # -- next rows: DDA tree, the emulated 8-rank allreduce ----------------------------------------------
     nt = 8 * 2 ** 20 // 16 * 2                            # 2 MiB of bf16 per rank
-    tree_sets = [[torch.randn(nt, device=dev).to(torch.bfloat16) for _ in range(N)] for _ in range(S)]
-    tree_chunks = [[torch.empty(nt // N, dtype=torch.bfloat16, device=dev) for _ in range(N)] for _ in range(S)]
-    tree_out = [torch.empty(nt, dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    ST = cold_copies(nt * 2)                               # each phase reads 2 MiB
+    tree_src = torch.randn(nt, device=dev).to(torch.bfloat16)
+    tree_sets = [[tree_src.clone() for _ in range(N)] for _ in range(ST)]
+    tree_chunks = [[torch.empty(nt // N, dtype=torch.bfloat16, device=dev) for _ in range(N)] for _ in range(ST)]
+    tree_out = [torch.empty(nt, dtype=torch.bfloat16, device=dev) for _ in range(ST)]
     kernels["dda_tree_rs_bf16_2MiB"] = timer.measure(
-        lambda i: lpc.dda_tree_reduce_scatter(tree_sets[i % S], 0, tree_chunks[i % S][0]), B, L, WB,
+        lambda i: lpc.dda_tree_reduce_scatter(tree_sets[i % ST], 0, tree_chunks[i % ST][0]), B, L, WB,
         N * (nt // N) * 2 + (nt // N) * 2)
     kernels["dda_tree_ag_bf16_2MiB"] = timer.measure(
-        lambda i: lpc.dda_tree_allgather(tree_chunks[i % S], tree_out[i % S]), B, L, WB, nt * 2 * 2)
-    del tree_sets, tree_chunks, tree_out
+        lambda i: lpc.dda_tree_allgather(tree_chunks[i % ST], tree_out[i % ST]), B, L, WB, nt * 2 * 2)
+    del tree_src, tree_sets, tree_chunks, tree_out
     for algo, name, dt in ((lpc.ALGO_LOW_PRECISION, "low_precision", f32),
                            (lpc.ALGO_DDA_TREE, "dda_tree", f32)):
-        ar_bufs = [[torch.empty(n, dtype=dt, device=dev) for _ in range(N)] for _ in range(4)]
+        ar_bufs = [[torch.empty(n, dtype=dt, device=dev) for _ in range(N)] for _ in range(cold_copies(N * n * 4))]
         for bl in ar_bufs:
             for t in bl:
                 t.copy_(xs[0])
@@ -571,8 +603,8 @@ def main():
         del ar_bufs, ws
     # the small-message allreduce: DDA flat over the 8 emulated ranks at 64 KiB bf16 per rank
     m64 = inputs.HIDDEN * 4
-    flat_sets = [[torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[4]]
-                 for _ in range(16)]
+    flat_src = [torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in dda_host[4]]
+    flat_sets = [[t.clone() for t in flat_src] for _ in range(cold_copies(N * m64 * 2))]
     ws_flat = torch.empty(lpc.lpc_allreduce_workspace_bytes(lpc.ALGO_DDA_FLAT, N, m64, torch.bfloat16),
                           dtype=u8, device=dev)
     r = timer.measure(lambda i: lpc.lpc_allreduce_emulated(flat_sets[i % len(flat_sets)], lpc.ALGO_DDA_FLAT,
@@ -590,11 +622,11 @@ def main():
     # -- extra per-kernel lines: 256 MiB bf16 per rank, fused by size, all-to-all-v rows -------------------
     if not args.no_extra:
         log("256 MiB bf16 per rank (device-generated), fused by size, all-to-all-v rows")
-        # Two copies of each large workload, used in turn: one copy (about 1.4 GiB for the 256 MiB
-        # fused launch) already exceeds the 256 MB Infinity Cache.
-        COPIES = 2
+        # Copies of each large workload, used in turn, so that 1 GiB is read between two reads of
+        # one copy (the fused launch reads 248 MB of each).
         n4 = inputs.WORKLOADS[inputs.LP_256MIB_BF16]["n"]
         C4 = n4 // N
+        COPIES = cold_copies(fused_read_bytes(n4, N))
         sets4 = []
         for k in range(COPIES):
             b4 = fused_set(torch, dev, n4, N, torch.bfloat16)
@@ -634,12 +666,11 @@ def main():
         torch.cuda.empty_cache()
 
         # The fused kernel against message size: fp32, N=8, values as in the 16 MiB workload.  The
-        # launch's fixed cost weighs less as the message grows.  Copies are cycled so that together
-        # they hold at least three times the Infinity Cache.
+        # launch's fixed cost weighs less as the message grows.  Copies cycled for cold HBM.
         sizes = {}
-        for mib in (16, 32, 64, 128):
+        for mib in (4, 8, 16, 32, 64, 128):
             ns = mib * 2 ** 20 // 4
-            copies = max(2, -(-3 * MALL_BYTES // sum(fused_layout(ns, N, 4))))
+            copies = cold_copies(fused_read_bytes(ns, N))
             sets_s = []
             for k in range(copies):
                 b_s = fused_set(torch, dev, ns, N, f32)
@@ -666,7 +697,7 @@ def main():
             d["frac"] = round(d["gbps"] / HBM_PEAK_GBPS, 4)
             d["copies"] = copies
             sizes["%dMiB" % mib] = d
-            for b in sets_s:
+            for b in sets_s[:3 * (WB + L)]:                      # the copies the timed batches used
                 assert torch.equal(b["oc"], sets_s[0]["cc"][0]), "fused %d MiB: reduced chunk differs" % mib
             del sets_s, b_s, fused_s
             torch.cuda.synchronize()
@@ -682,7 +713,8 @@ def main():
         perm = torch.empty(rows, dtype=torch.int32, device=dev)
         lpc.lpc_a2av_route(dest, N, counts, offsets, perm)
         sets5 = []
-        for k in range(COPIES):
+        COPIES5 = cold_copies(m5 + m5 // BLOCK * 4)          # the dequantize reads 118 MB of each copy
+        for k in range(COPIES5):
             a5 = Arena(torch, dev, [m5 * 2, m5, m5 // BLOCK * 4, m5 * 2])
             b5 = dict(x=a5.take(m5, torch.bfloat16).view(rows, row_len),
                       codes=a5.take(m5, u8).view(rows, row_len),
@@ -697,12 +729,12 @@ def main():
         kernels["a2av_route_16384"] = timer.measure(
             lambda i: lpc.lpc_a2av_route(dest, N, counts, offsets, perm), 3, 20, 2, rows * 4 * 2 + N * 8)
         kernels["a2av_quantize_rows_bf16"] = timer.measure(
-            lambda i: lpc.lpc_quantize_fp8_rows(sets5[i % COPIES]["x"], perm, sets5[i % COPIES]["codes"],
-                                                sets5[i % COPIES]["scales"]), 3, 20, 2,
+            lambda i: lpc.lpc_quantize_fp8_rows(sets5[i % COPIES5]["x"], perm, sets5[i % COPIES5]["codes"],
+                                                sets5[i % COPIES5]["scales"]), 3, 20, 2,
             quantize_bytes(m5, 2) + rows * 4)
         kernels["a2av_dequantize_bf16"] = timer.measure(
-            lambda i: lpc.lpc_dequantize_fp8(sets5[i % COPIES]["codes"], sets5[i % COPIES]["scales"],
-                                             sets5[i % COPIES]["back"]), 3, 20, 2, m5 + m5 // BLOCK * 4 + m5 * 2)
+            lambda i: lpc.lpc_dequantize_fp8(sets5[i % COPIES5]["codes"], sets5[i % COPIES5]["scales"],
+                                             sets5[i % COPIES5]["back"]), 3, 20, 2, m5 + m5 // BLOCK * 4 + m5 * 2)
         del sets5, b5, a5
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -715,7 +747,7 @@ def main():
             lpc.lpc_measure_stream(src, 64 * 2 ** 20, dst, 64 * 2 ** 20)
         torch.cuda.synchronize()
 
-    traffic = traffic_from_profiles("rs_ag_fused_kernel<8,float>")
+    traffic = traffic_from_profiles("rs_ag_fused_kernel<8,float,2>")
     result = {
         "metric": "FP8 RS+AG reduce GB/s & % of HBM peak (16MB/rank, N=8); DDA-flat µs @64KB",
         "value": round(value, 2),
@@ -735,9 +767,11 @@ def main():
                         "scales; DDA-flat reduce of 8 x 32,768 bf16",
             "nranks": N, "elems_per_rank": n, "block": BLOCK,
             "step": "quantize + fused RS+AG + DDA flat 64 KiB",
-            "buffer_sets": S, "set_bytes": set_bytes, "hbm_resident": True,
+            "buffer_sets": S, "quantize_buffer_sets": SQ, "set_bytes": set_bytes, "hbm_resident": True,
+            "cold_read_bytes": COLD_READ_BYTES,
             "timing": "kernels: %d batches of %d warm-up + %d launches back to back behind a spin kernel, "
-                      "each batch after a read-only pass over 1 GiB, HIP events on the launch stream; "
+                      "each batch after a read-only pass over 1 GiB, HIP events on the launch stream, buffer "
+                      "copies cycled so that 1 GiB is read between two reads of one copy (cold HBM); "
                       "step: W warm-up + K steps back to back behind a spin kernel, HIP events" % (B, WB, L),
         },
         "roofline": {
@@ -747,7 +781,7 @@ def main():
             "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "rs_ag_fused_kernel<8,float>",
+            "kernel": "rs_ag_fused_kernel<8,float,2>",
             "bytes_per_launch": fb,
             "read_bytes_per_launch": fr,
             "write_bytes_per_launch": fw,

@@ -293,108 +293,130 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, v
 }
 
 // ---------------------------------------------------------------------------
-// (2)+(3) fused.  Every lane owns the same position i of every chunk.  The
-// peers' chunks (peer q = rank + 1 .. rank + N - 1, mod N) are split into
-// slices of P = kPeersPerSlice: grid.y == 0 reduces and requantizes the own
-// chunk at i, writes its dequantization from registers, and dequantizes peers
-// q = 1 .. P at i; grid.y == y > 0 dequantizes peers q = P*y + 1 .. P*y + P.
-// One peer per slice measured fastest: 2, 3 or 7 per slice, or a slice 0 that
-// takes no peer, were 1-10% slower at 16 MiB fp32 and 256 MiB bf16.  Each lane
-// issues all of its loads before its first conversion.  With bf16 output
-// (W = 8) the code loads are non-temporal: 15 streams are read once each, and
-// keeping them out of the caches measured faster at large sizes.
+// (2)+(3) fused.  Every lane owns the same positions of every chunk.  The
+// peers' chunks (peer q = rank + 1 .. rank + N - 1, mod N) go one per slice:
+// grid.y == 0 reduces and requantizes the own chunk at the lane's positions,
+// writes its dequantization from registers, and dequantizes peer rank + 1
+// there; grid.y == y > 0 dequantizes peer rank + y + 1.  A slice has `lanes`
+// = C / W lane vectors; a lane owns V of them, H = lanes / V apart, and issues
+// every load of all V before its first conversion.  All code loads are
+// non-temporal: each stream is read once.
+//
+// On cold HBM a lane's first conversion waits a full load latency, so the
+// launch is bound by how many latencies lie on its path.  One vector per lane
+// at 16 MiB fp32 and N = 8 is 14,336 wavefronts, two rounds of what the GPU
+// holds at once (8 per SIMD): 6.7 us.  Two vectors per lane (V = 2) make it
+// one round of 7,168 wavefronts: 5.4 us.  Where one vector per lane already
+// fits in one round (8 MiB and below), V = 1 is faster, and with bf16 output
+// (W = 8) V = 2 measured no faster at 16-256 MiB.  Slice 0 keeps a peer: a
+// slice for the reduction alone, or two or more peers per slice, measured
+// 2-14% slower.
 // ---------------------------------------------------------------------------
 
-constexpr int kPeersPerSlice = 1;
+// Wavefronts a full MI355X runs at once at 8 per SIMD (256 CUs x 4 SIMDs).
+constexpr size_t kRoundWaves = 8192;
 
-__host__ __device__ constexpr int fused_slices(int N) {
-    return N <= 1 ? 1 : (N - 1 + kPeersPerSlice - 1) / kPeersPerSlice;
-}
+__host__ __device__ constexpr int fused_slices(int N) { return N <= 1 ? 1 : N - 1; }
 
-template <int N, typename Out>
+template <int N, typename Out, int V>
 __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, RankCodes peers, int rank,
-                                                               size_t C, uint8_t* __restrict__ cc,
+                                                               size_t C, size_t H, uint8_t* __restrict__ cc,
                                                                float* __restrict__ cs,
                                                                Out* __restrict__ out) {
     constexpr int W = lane_width<Out>();
-    constexpr bool kNtLoads = W == 8;
     using Codes = typename LaneCodes<W>::T;
-    const size_t i = lane_elem<W>();
-    if (i >= C) return;
+    const size_t L = xcd_tile() * kThreads + threadIdx.x;
+    if (L >= H) return;  // whole blocks of 128/W lanes drop out together (H % (128/W) == 0)
     const int y = blockIdx.y;
-    const int q_first = kPeersPerSlice * y + 1;
-    Codes pc[kPeersPerSlice];
-    float ps[kPeersPerSlice];
-    int pp[kPeersPerSlice];
-#pragma unroll
-    for (int k = 0; k < kPeersPerSlice; ++k) {
-        int p = rank + q_first + k;
-        if (p >= N) p -= N;
-        pp[k] = p;
-    }
+    int q = rank + y + 1;  // this slice's peer
+    if (q >= N) q -= N;
+    Codes pc[V];
+    float ps[V];
     float d[W];
     if (y == 0) {
-        const size_t own = (size_t)rank * C + i;
-        Codes c[N];
-        float s[N];
+        Codes c[V][N];
+        float s[V][N];
 #pragma unroll
-        for (int p = 0; p < N; ++p) {
-            c[p] = load_codes<W, kNtLoads>(in.codes[p] + own);
-            s[p] = in.scales[p][own / kBlock];
-        }
+        for (int k = 0; k < V; ++k) {
+            const size_t own = (size_t)rank * C + (L + k * H) * W;
 #pragma unroll
-        for (int k = 0; k < kPeersPerSlice; ++k) {
-            if (q_first + k < N) {
-                pc[k] = load_codes<W, kNtLoads>(peers.codes[pp[k]] + i);
-                ps[k] = peers.scales[pp[k]][i / kBlock];
+            for (int p = 0; p < N; ++p) {
+                c[k][p] = load_codes<W, true>(in.codes[p] + own);
+                s[k][p] = in.scales[p][own / kBlock];
             }
         }
-        float acc[W];
-        dequant_lane(c[0], s[0], acc);
+        if constexpr (N > 1) {
 #pragma unroll
-        for (int p = 1; p < N; ++p) {
-            dequant_lane(c[p], s[p], d);
-#pragma unroll
-            for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
+            for (int k = 0; k < V; ++k) {
+                const size_t i = (L + k * H) * W;
+                pc[k] = load_codes<W, true>(peers.codes[q] + i);
+                ps[k] = peers.scales[q][i / kBlock];
+            }
         }
-        float sc;
-        const Codes code = quantize_lane(acc, &sc);
-        store_codes<W>(cc + i, code);
-        if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = sc;
-        dequant_lane(code, sc, d);  // own chunk straight from registers
-        store_lane_nt(out + own, d);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const size_t i = (L + k * H) * W;
+            const size_t own = (size_t)rank * C + i;
+            float acc[W];
+            dequant_lane(c[k][0], s[k][0], acc);
+#pragma unroll
+            for (int p = 1; p < N; ++p) {
+                dequant_lane(c[k][p], s[k][p], d);
+#pragma unroll
+                for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
+            }
+            float sc;
+            const Codes code = quantize_lane(acc, &sc);
+            store_codes<W>(cc + i, code);
+            if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = sc;
+            dequant_lane(code, sc, d);  // own chunk straight from registers
+            store_lane_nt(out + own, d);
+        }
+        if constexpr (N == 1) return;
     } else {
 #pragma unroll
-        for (int k = 0; k < kPeersPerSlice; ++k) {
-            if (q_first + k < N) {
-                pc[k] = load_codes<W, kNtLoads>(peers.codes[pp[k]] + i);
-                ps[k] = peers.scales[pp[k]][i / kBlock];
-            }
+        for (int k = 0; k < V; ++k) {
+            const size_t i = (L + k * H) * W;
+            pc[k] = load_codes<W, true>(peers.codes[q] + i);
+            ps[k] = peers.scales[q][i / kBlock];
         }
     }
 #pragma unroll
-    for (int k = 0; k < kPeersPerSlice; ++k) {
-        if (q_first + k < N) {
-            dequant_lane(pc[k], ps[k], d);
-            store_lane_nt(out + (size_t)pp[k] * C + i, d);
-        }
+    for (int k = 0; k < V; ++k) {
+        const size_t i = (L + k * H) * W;
+        dequant_lane(pc[k], ps[k], d);
+        store_lane_nt(out + (size_t)q * C + i, d);
     }
+}
+
+// Lane vectors per lane of the fused launch: 2 for fp32 output when one per lane would take more
+// than one round of wavefronts and the slice splits into two halves of whole blocks (C % 256 == 0),
+// else 1.
+static int fused_vectors(int nranks, size_t C, int out_bf16) {
+    if (out_bf16 || C % (2 * kBlock) != 0) return 1;
+    const size_t wgs = (C / lane_width<float>() + kThreads - 1) / kThreads * fused_slices(nranks);
+    return wgs * (kThreads / 64) > kRoundWaves ? 2 : 1;
+}
+
+template <int N, typename Out, int V>
+static hipError_t launch_fused_v(const RankCodes& in, const RankCodes& peers, int rank, size_t C, uint8_t* cc,
+                                 float* cs, void* out, hipStream_t stream) {
+    const size_t H = C / lane_width<Out>() / V;
+    const dim3 grid((unsigned)((H + kThreads - 1) / kThreads), fused_slices(N));
+    return launch(rs_ag_fused_kernel<N, Out, V>, grid, dim3(kThreads), 0, stream, in, peers, rank, C, H, cc, cs,
+                  static_cast<Out*>(out));
 }
 
 hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int nranks, int rank, size_t n,
                               uint8_t* cc, float* cs, void* out, int out_bf16, hipStream_t stream) {
     const size_t C = n / nranks;
-    const dim3 block(kThreads);
-    const dim3 grid_f32 = lane_grid<lane_width<float>()>(C, fused_slices(nranks));
-    const dim3 grid_bf16 = lane_grid<lane_width<uint16_t>()>(C, fused_slices(nranks));
+    const bool two = fused_vectors(nranks, C, out_bf16) == 2;
     switch (nranks) {
-#define LPC_FUSED_CASE(NR)                                                                                      \
-    case NR:                                                                                                    \
-        if (out_bf16)                                                                                           \
-            return launch(rs_ag_fused_kernel<NR, uint16_t>, grid_bf16, block, 0, stream, in, peers, rank, C, cc, \
-                          cs, static_cast<uint16_t*>(out));                                                     \
-        return launch(rs_ag_fused_kernel<NR, float>, grid_f32, block, 0, stream, in, peers, rank, C, cc, cs,     \
-                      static_cast<float*>(out));
+#define LPC_FUSED_CASE(NR)                                                                              \
+    case NR:                                                                                            \
+        if (out_bf16) return launch_fused_v<NR, uint16_t, 1>(in, peers, rank, C, cc, cs, out, stream); \
+        if (two) return launch_fused_v<NR, float, 2>(in, peers, rank, C, cc, cs, out, stream);          \
+        return launch_fused_v<NR, float, 1>(in, peers, rank, C, cc, cs, out, stream);
         LPC_FUSED_CASE(1) LPC_FUSED_CASE(2) LPC_FUSED_CASE(3) LPC_FUSED_CASE(4)
         LPC_FUSED_CASE(5) LPC_FUSED_CASE(6) LPC_FUSED_CASE(7) LPC_FUSED_CASE(8)
 #undef LPC_FUSED_CASE

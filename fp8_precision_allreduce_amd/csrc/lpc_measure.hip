@@ -19,46 +19,63 @@ constexpr int kThreads = 256;
 using lpc::u32x4_t;
 
 // Lane g of L launched lanes loads 16-byte vectors g, g + L, ..., g + (KR-1)*L
-// of src (those below nr) and stores 16-byte vectors g, g + L, ..., of dst
-// (those below nw), non-temporally, so that every wavefront instruction
-// covers one contiguous KiB.  The stored value depends on every loaded one.
-// Tiles in XCD-aware order, as the library's kernels take them.
+// of src (those below nr) and then stores 16-byte vectors g, g + L, ..., of dst
+// (those below nw), loads and stores non-temporal, so that every wavefront
+// instruction covers one contiguous KiB.  The stored value depends on every
+// loaded one; with nothing to store, a store under a flag that the host always
+// passes as 0 keeps the loads live.  Tiles in XCD-aware order, as the
+// library's kernels take them.
 template <int KR, int KW>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const uint4* __restrict__ src, size_t nr,
-                                                          uint4* __restrict__ dst, size_t nw) {
+                                                          uint4* __restrict__ dst, size_t nw, int* sink,
+                                                          int dump) {
     const size_t L = (size_t)gridDim.x * kThreads;
     const size_t g = lpc::xcd_tile() * kThreads + threadIdx.x;
-    uint4 v = make_uint4((uint32_t)g, 0u, 0u, 0u);
+    u32x4_t v = {(uint32_t)g, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
         const size_t i = g + k * L;
-        if (i < nr) {
-            const uint4 t = src[i];
-            v.x ^= t.x;
-            v.y ^= t.y;
-            v.z ^= t.z;
-            v.w ^= t.w;
-        }
+        if (i < nr) v ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
     }
+    if constexpr (KW == 0) {
+        if (dump) *sink = (int)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < KW; ++k) {
-        const size_t i = g + k * L;
-        if (i < nw) {
-            const u32x4_t w = {v.x, v.y, v.z, v.w ^ (uint32_t)k};
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(dst + i));
+        for (int k = 0; k < KW; ++k) {
+            const size_t i = g + k * L;
+            if (i < nw) {
+                u32x4_t w = v;
+                w[3] ^= (uint32_t)k;
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(dst + i));
+            }
         }
     }
 }
 
 template <int KR, int KW>
-hipError_t launch_stream(const void* src, size_t nr, void* dst, size_t nw, hipStream_t stream) {
-    const size_t lanes = std::max((nr + KR - 1) / KR, (nw + KW - 1) / KW);
-    const dim3 grid((unsigned)((lanes + kThreads - 1) / kThreads));
+hipError_t launch_stream(const void* src, size_t nr, void* dst, size_t nw, unsigned wgs, int* sink,
+                         hipStream_t stream) {
     const uint4* s = static_cast<const uint4*>(src);
     uint4* d = static_cast<uint4*>(dst);
-    void* args[] = {&s, &nr, &d, &nw};
-    return hipLaunchKernel(reinterpret_cast<const void*>(stream_kernel<KR, KW>), grid, dim3(kThreads), args, 0,
+    int dump = 0;
+    void* args[] = {&s, &nr, &d, &nw, &sink, &dump};
+    return hipLaunchKernel(reinterpret_cast<const void*>(stream_kernel<KR, KW>), dim3(wgs), dim3(kThreads), args, 0,
                            stream);
+}
+
+// Per-lane counts are rounded up to 1, 2, 4 or 8 (0 when there is nothing to move).
+int bucket(size_t k) { return k == 0 ? 0 : k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8; }
+
+// Workgroups of the streaming kernel: one round of resident wavefronts (2,048 workgroups of 256
+// lanes, 8 wavefronts per SIMD on 256 CUs) when that leaves at most 8 vectors per lane each way,
+// fewer when there is less to move, more (8 vectors per lane) for larger transfers.
+size_t stream_workgroups(size_t nr, size_t nw) {
+    constexpr size_t kRound = 2048, kMaxPerLane = 8;
+    const size_t m = std::max(nr, nw);
+    const size_t need = (m + kThreads - 1) / kThreads;
+    if (need <= kRound) return need;
+    if (m <= kRound * kThreads * kMaxPerLane) return kRound;
+    return (m + kThreads * kMaxPerLane - 1) / (kThreads * kMaxPerLane);
 }
 
 // A kernel-argument block of K bytes.
@@ -97,23 +114,26 @@ lpc_status lpc_measure_stream(const void* src, size_t read_bytes, void* dst, siz
                               hipStream_t stream) {
     if (read_bytes % 16 || write_bytes % 16) return LPC_ERR_SHAPE;
     if (read_bytes == 0 && write_bytes == 0) return LPC_OK;
-    if ((read_bytes && !src) || (write_bytes && !dst)) return LPC_ERR_NULL;
-    if ((read_bytes && misaligned(src)) || (write_bytes && misaligned(dst))) return LPC_ERR_ALIGN;
+    if ((read_bytes && !src) || !dst) return LPC_ERR_NULL;
+    if ((read_bytes && misaligned(src)) || misaligned(dst)) return LPC_ERR_ALIGN;
+    int* sink = static_cast<int*>(dst);  // read only: never written
     const size_t nr = read_bytes / 16, nw = write_bytes / 16;
-    // loads and stores per lane in the ratio of the two byte counts, 1..4 each
-    int kr = 1, kw = 1;
-    if (nr >= nw) kr = nw == 0 ? 4 : (int)std::min<size_t>(4, (nr + nw / 2) / nw);
-    else kw = nr == 0 ? 4 : (int)std::min<size_t>(4, (nw + nr / 2) / nr);
-    if (std::max((nr + kr - 1) / kr, (nw + kw - 1) / kw) > (size_t)INT32_MAX) return LPC_ERR_SHAPE;
+    const size_t wgs = stream_workgroups(nr, nw);
+    if (wgs > (size_t)INT32_MAX / kThreads) return LPC_ERR_SHAPE;
+    const size_t L = wgs * kThreads;
+    const int kr = bucket((nr + L - 1) / L), kw = bucket((nw + L - 1) / L);
+    const unsigned g = (unsigned)wgs;
     hipError_t e = hipErrorInvalidValue;
-    switch (kr * 8 + kw) {
-        case 1 * 8 + 1: e = launch_stream<1, 1>(src, nr, dst, nw, stream); break;
-        case 2 * 8 + 1: e = launch_stream<2, 1>(src, nr, dst, nw, stream); break;
-        case 3 * 8 + 1: e = launch_stream<3, 1>(src, nr, dst, nw, stream); break;
-        case 4 * 8 + 1: e = launch_stream<4, 1>(src, nr, dst, nw, stream); break;
-        case 1 * 8 + 2: e = launch_stream<1, 2>(src, nr, dst, nw, stream); break;
-        case 1 * 8 + 3: e = launch_stream<1, 3>(src, nr, dst, nw, stream); break;
-        case 1 * 8 + 4: e = launch_stream<1, 4>(src, nr, dst, nw, stream); break;
+    switch (kr * 16 + kw) {
+#define LPC_STREAM_CASE(R, W) \
+    case R * 16 + W: e = launch_stream<R, W>(src, nr, dst, nw, g, sink, stream); break;
+        LPC_STREAM_CASE(1, 0) LPC_STREAM_CASE(2, 0) LPC_STREAM_CASE(4, 0) LPC_STREAM_CASE(8, 0)
+        LPC_STREAM_CASE(0, 1) LPC_STREAM_CASE(0, 2) LPC_STREAM_CASE(0, 4) LPC_STREAM_CASE(0, 8)
+        LPC_STREAM_CASE(1, 1) LPC_STREAM_CASE(1, 2) LPC_STREAM_CASE(1, 4) LPC_STREAM_CASE(1, 8)
+        LPC_STREAM_CASE(2, 1) LPC_STREAM_CASE(2, 2) LPC_STREAM_CASE(2, 4) LPC_STREAM_CASE(2, 8)
+        LPC_STREAM_CASE(4, 1) LPC_STREAM_CASE(4, 2) LPC_STREAM_CASE(4, 4) LPC_STREAM_CASE(4, 8)
+        LPC_STREAM_CASE(8, 1) LPC_STREAM_CASE(8, 2) LPC_STREAM_CASE(8, 4) LPC_STREAM_CASE(8, 8)
+#undef LPC_STREAM_CASE
     }
     return e == hipSuccess ? LPC_OK : LPC_ERR_HIP;
 }

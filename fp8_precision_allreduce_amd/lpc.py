@@ -286,11 +286,12 @@ def lpc_allreduce_emulated_noalloc(bufs, algo: int, stream=None):
 
 
 def lpc_measure_stream(src, read_bytes: int, dst, write_bytes: int, stream=None):
-    """Plain streaming kernel (measurement reference): reads read_bytes of src, writes write_bytes of dst."""
+    """Plain streaming kernel (measurement reference): reads read_bytes of src, writes write_bytes
+    of dst (with write_bytes == 0, dst is a never-written sink of at least 16 bytes)."""
     if src is not None and src.numel() * src.element_size() < read_bytes:
         raise ValueError("src holds fewer than %d bytes" % read_bytes)
-    if dst is not None and dst.numel() * dst.element_size() < write_bytes:
-        raise ValueError("dst holds fewer than %d bytes" % write_bytes)
+    if dst is not None and dst.numel() * dst.element_size() < max(write_bytes, 16 if read_bytes else 0):
+        raise ValueError("dst holds fewer than %d bytes" % max(write_bytes, 16))
     _call("lpc_measure_stream", _dev(src, "src") if src is not None else None, read_bytes,
           _dev(dst, "dst") if dst is not None else None, write_bytes, _stream(stream))
 

@@ -29,13 +29,18 @@ extern "C" {
 
 /* Plain streaming kernel: reads read_bytes from src and writes write_bytes
  * to dst (the written values depend on the read ones; their content is
- * otherwise unspecified).  16-byte loads and non-temporal 16-byte stores;
- * each lane makes KR loads and KW stores (1..4 each, in the ratio of the two
- * byte counts), every wavefront instruction covering one contiguous KiB, and
- * tiles in the XCD-aware order of the library's kernels.
+ * otherwise unspecified).  16-byte non-temporal loads and stores, every
+ * wavefront instruction covering one contiguous KiB, tiles in the XCD-aware
+ * order of the library's kernels.  The grid is one round of resident
+ * wavefronts (2,048 workgroups of 256 lanes) or fewer; a lane makes up to 8
+ * loads, then up to 8 stores, at a stride of the grid's lane count (larger
+ * transfers take more workgroups at 8 per lane).  Measured on cold HBM this
+ * was the fastest of the grid sizes and load kinds tried.
  *   src  [read_bytes], device, 16-byte aligned (may be NULL if read_bytes is 0)
- *   dst  [write_bytes], device, 16-byte aligned (may be NULL if write_bytes is 0);
- *        must not overlap src
+ *   dst  [write_bytes], device, 16-byte aligned, must not overlap src.  With
+ *        write_bytes == 0 it must still point to 16 valid bytes, which are not
+ *        written (the kernel's store to it sits under a flag that is always off,
+ *        which keeps the loads live)
  *   read_bytes, write_bytes  multiples of 16 (else LPC_ERR_SHAPE); both 0 is a no-op */
 lpc_status lpc_measure_stream(const void *src, size_t read_bytes, void *dst, size_t write_bytes,
                               hipStream_t stream);

@@ -66,6 +66,7 @@ def test_measure_errors(L):
     assert s(None, 0, None, 0, None) == OK
     assert s(None, 16, A, 16, None) == NULL
     assert s(A, 16, None, 16, None) == NULL
+    assert s(A, 16, None, 0, None) == NULL                 # read only: dst is the sink
     assert s(B, 16, A, 16, None) == ALIGN
     assert s(A, 16, B, 16, None) == ALIGN
     assert s(A, 16, A + 1024, 32, None) == HIP            # passes the checks; no device

@@ -1,6 +1,7 @@
 """The measurement reference kernels (include/lpc_measure.h) on the GPU: the plain
 streaming kernel writes exactly its destination range with the documented values and
-nothing past it, for every load:store ratio it picks; the empty launch writes nothing."""
+nothing past it, for every load:store count it picks (and nothing at all when it only
+reads); the empty launch writes nothing."""
 import numpy as np
 import pytest
 import torch
@@ -23,17 +24,25 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
+def _layout(nr: int, nw: int):
+    """(lanes L, loads per lane KR, stores per lane KW) the stream kernel picks: one round
+    of 2,048 workgroups of 256 lanes when that leaves at most 8 vectors per lane each way,
+    fewer workgroups when there is less to move, more at 8 per lane beyond; per-lane counts
+    rounded up to 1, 2, 4 or 8."""
+    m = max(nr, nw)
+    need = -(-m // 256)
+    wgs = need if need <= 2048 else (2048 if m <= 2048 * 256 * 8 else -(-m // (256 * 8)))
+    L = wgs * 256
+    bucket = lambda k: 0 if k == 0 else 1 if k <= 1 else 2 if k <= 2 else 4 if k <= 4 else 8
+    return L, bucket(-(-nr // L)), bucket(-(-nw // L))
+
+
 def _expected(src_words: np.ndarray, nr: int, nw: int) -> np.ndarray:
     """The stream kernel's output as uint32 words [nw, 4], computed on the host from the
     kernel's documented lane layout: lane g of L lanes loads 16-byte vectors g + k*L (k < KR,
     below nr), xors them into (g, 0, 0, 0), and stores the result with its last word xored
     with k at vectors g + k*L (k < KW, below nw)."""
-    if nr >= nw:
-        kr, kw = (4 if nw == 0 else min(4, (nr + nw // 2) // nw)), 1
-    else:
-        kr, kw = 1, (4 if nr == 0 else min(4, (nw + nr // 2) // nr))
-    lanes = max(-(-nr // kr), -(-nw // kw))
-    L = -(-lanes // 256) * 256
+    L, kr, kw = _layout(nr, nw)
     v = np.zeros((L, 4), np.uint32)
     v[:, 0] = np.arange(L, dtype=np.uint32)
     src = src_words.reshape(-1, 4)
@@ -52,9 +61,10 @@ def _expected(src_words: np.ndarray, nr: int, nw: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("rb,wb", [(1 << 20, 1 << 20), (8_110_080, 17_317_888), (16 << 20, 4_325_376),
-                                   (16 * 1000, 16 * 3000), (16 * 4096, 16), (0, 16 * 777), (16 * 513, 0)],
+                                   (16 * 1000, 16 * 3000), (16 * 4096, 16), (0, 16 * 777), (16 * 513, 0),
+                                   (64 << 20, 16), (48 << 20, 40 << 20)],
                          ids=["copy", "fused_mix", "quantize_mix", "ragged_1to3", "read_heavy", "write_only",
-                              "read_only"])
+                              "read_only", "read_64MiB_beyond_one_round", "copy_48_40MiB"])
 def test_stream_writes_its_range(dev, rb, wb):
     say("measure stream read=%d write=%d" % (rb, wb))
     g = np.random.Generator(np.random.PCG64(rb + 7 * wb))
@@ -62,11 +72,12 @@ def test_stream_writes_its_range(dev, rb, wb):
     src = torch.from_numpy(src_h.view(np.int32)).to(dev)
     dst = torch.full(((wb + 2 * GUARD) // 4,), -1, dtype=torch.int32, device=dev)
     body = dst[GUARD // 4:(GUARD + wb) // 4]
-    lpc.lpc_measure_stream(src if rb else None, rb, body if wb else None, wb)
+    # with nothing to write, dst is the never-written sink: the guard-filled words must stay
+    lpc.lpc_measure_stream(src if rb else None, rb, body if wb else dst[GUARD // 4:GUARD // 4 + 4], wb)
     torch.cuda.synchronize()
     got = dst.cpu().numpy().view(np.uint32)
     assert np.all(got[:GUARD // 4] == 0xFFFFFFFF) and np.all(got[(GUARD + wb) // 4:] == 0xFFFFFFFF), \
-        "the stream kernel wrote outside its destination"
+        "the stream kernel wrote outside its destination (or into the read-only sink)"
     if wb:
         exp = _expected(src_h[:rb // 4], rb // 16, wb // 16)
         assert np.array_equal(got[GUARD // 4:(GUARD + wb) // 4].reshape(-1, 4), exp)

@@ -351,6 +351,20 @@ def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "chunk_blocks=%d" % chunk_blocks)
 
 
+@pytest.mark.parametrize("N,C", [(2, 2097408), (3, 1048832), (5, 524544), (8, 524416)],
+                         ids=["N2", "N3", "N5", "N8-odd-blocks"])
+def test_fused_grid_beyond_one_round(dev, orc, N, C):
+    """Chunks just past the size where one lane vector per lane would take more than
+    one round of wavefronts (8,192): the fp32 fused launch gives each lane two vectors,
+    half a chunk apart (N = 2, 3, 5); with an odd number of blocks per chunk (N = 8) it
+    keeps one.  Every rank's fused launch, every intermediate, in full."""
+    n = C * N
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r, n) for r in range(N)]
+    say("fused beyond one round: N=%d C=%d n=%d" % (N, C, n))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, True)
+    compare_allreduce(res, orc.lp_allreduce(xs), "N=%d C=%d" % (N, C))
+
+
 def test_quantize_and_dequantize_at_the_largest_size(dev, orc):
     """n = LPC_MAX_ELEMS (2^32 fp32 elements, 16 GiB): quantize and dequantize at
     the largest accepted size, where byte offsets pass 2^32 and the grid is at its
