@@ -126,14 +126,14 @@ def cold_copies(read_bytes: int) -> int:
 
 
 def fused_grid(n: int, N: int, out_size: int):
-    """(grid_x, grid_y) of the fused launch, as the library picks it: one slice per peer, one
-    lane vector per lane, or two (half a chunk apart) for fp32 output when one per lane would
-    take more than one round of wavefronts and the chunk is a multiple of 256 elements."""
+    """(grid_x, grid_y) of the fused launch, as the library picks it: V lane vectors per lane, V
+    slices for the reduction and one per other peer.  V = 2 for fp32 output when one per lane
+    would take more than one round of wavefronts and the chunk is a multiple of 256 elements."""
     C = n // N
     lanes = C // (16 // out_size)
-    slices = max(1, N - 1)
-    v = 2 if (out_size == 4 and C % 256 == 0 and -(-lanes // THREADS) * slices * 4 > ROUND_WAVES) else 1
-    return -(-(lanes // v) // THREADS), slices
+    others = max(0, N - 2)
+    v = 2 if (out_size == 4 and C % 256 == 0 and -(-lanes // THREADS) * (1 + others) * 4 > ROUND_WAVES) else 1
+    return -(-(lanes // v) // THREADS), v + others
 
 
 KERNEL_SOURCES = ("lpc_device.hpp", "lpc_kernels.hip")   # every path kernel's device code lives in these two

@@ -293,30 +293,33 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, v
 }
 
 // ---------------------------------------------------------------------------
-// (2)+(3) fused.  Every lane owns the same positions of every chunk.  The
-// peers' chunks (peer q = rank + 1 .. rank + N - 1, mod N) go one per slice:
-// grid.y == 0 reduces and requantizes the own chunk at the lane's positions,
-// writes its dequantization from registers, and dequantizes peer rank + 1
-// there; grid.y == y > 0 dequantizes peer rank + y + 1.  A slice has `lanes`
-// = C / W lane vectors; a lane owns V of them, H = lanes / V apart, and issues
-// every load of all V before its first conversion.  All code loads are
-// non-temporal: each stream is read once.
+// (2)+(3) fused.  A slice (grid.y) has H lanes, each owning lane vectors of W
+// elements; the chunk has lanes = C / W vectors, H = lanes / V.
+//   * Slices y < V reduce: lane t takes vector y*H + t of the own chunk,
+//     loads it from all N ranks, sums in rank order, requantizes, writes the
+//     requantized codes and their dequantization (from registers), and
+//     dequantizes peer rank + 1's chunk at the same vector.
+//   * Slice y >= V dequantizes peer rank + y - V + 2's chunk: lane t takes
+//     vectors t, t + H, ..., t + (V-1)*H.
+// Every lane issues all of its loads before its first conversion.  All code
+// loads are non-temporal: each stream is read once.
 //
 // On cold HBM a lane's first conversion waits a full load latency, so the
-// launch is bound by how many latencies lie on its path.  One vector per lane
-// at 16 MiB fp32 and N = 8 is 14,336 wavefronts, two rounds of what the GPU
-// holds at once (8 per SIMD): 6.7 us.  Two vectors per lane (V = 2) make it
-// one round of 7,168 wavefronts: 5.4 us.  Where one vector per lane already
-// fits in one round (8 MiB and below), V = 1 is faster, and with bf16 output
-// (W = 8) V = 2 measured no faster at 16-256 MiB.  Slice 0 keeps a peer: a
-// slice for the reduction alone, or two or more peers per slice, measured
-// 2-14% slower.
+// launch is bound by how many latencies lie on its path.  At 16 MiB fp32 and
+// N = 8 one vector per lane (V = 1) is 14,336 wavefronts, two rounds of what
+// the GPU holds at once (8 per SIMD): 6.7 us.  V = 2 is 8,192 wavefronts, one
+// round, with the reduction spread over two slices of one vector per lane:
+// 5.3 us (a reduction slice of two vectors per lane measured 5.4 us, a slice
+// for the reduction alone 6.0-6.2 us).  Where V = 1 already fits in one round
+// (8 MiB and below) it is faster, and with bf16 output (W = 8) V = 2 measured
+// no faster at 16-256 MiB.
 // ---------------------------------------------------------------------------
 
 // Wavefronts a full MI355X runs at once at 8 per SIMD (256 CUs x 4 SIMDs).
 constexpr size_t kRoundWaves = 8192;
 
-__host__ __device__ constexpr int fused_slices(int N) { return N <= 1 ? 1 : N - 1; }
+// slices of the fused launch: V reduction slices and one per peer other than rank + 1
+__host__ __device__ constexpr int fused_slices(int N, int V) { return V + (N > 2 ? N - 2 : 0); }
 
 template <int N, typename Out, int V>
 __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, RankCodes peers, int rank,
@@ -325,76 +328,70 @@ __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, Ran
                                                                Out* __restrict__ out) {
     constexpr int W = lane_width<Out>();
     using Codes = typename LaneCodes<W>::T;
-    const size_t L = xcd_tile() * kThreads + threadIdx.x;
-    if (L >= H) return;  // whole blocks of 128/W lanes drop out together (H % (128/W) == 0)
+    const size_t t = xcd_tile() * kThreads + threadIdx.x;
+    if (t >= H) return;  // whole blocks of 128/W lanes drop out together (H % (128/W) == 0)
     const int y = blockIdx.y;
-    int q = rank + y + 1;  // this slice's peer
+    float d[W];
+    if (y < V) {
+        const size_t i = ((size_t)y * H + t) * W;
+        const size_t own = (size_t)rank * C + i;
+        int q = rank + 1;
+        if (q >= N) q -= N;
+        Codes c[N], pc;
+        float s[N], ps;
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            c[p] = load_codes<W, true>(in.codes[p] + own);
+            s[p] = in.scales[p][own / kBlock];
+        }
+        if constexpr (N > 1) {
+            pc = load_codes<W, true>(peers.codes[q] + i);
+            ps = peers.scales[q][i / kBlock];
+        }
+        float acc[W];
+        dequant_lane(c[0], s[0], acc);
+#pragma unroll
+        for (int p = 1; p < N; ++p) {
+            dequant_lane(c[p], s[p], d);
+#pragma unroll
+            for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
+        }
+        float sc;
+        const Codes code = quantize_lane(acc, &sc);
+        store_codes<W>(cc + i, code);
+        if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = sc;
+        dequant_lane(code, sc, d);  // own chunk straight from registers
+        store_lane_nt(out + own, d);
+        if constexpr (N > 1) {
+            dequant_lane(pc, ps, d);
+            store_lane_nt(out + (size_t)q * C + i, d);
+        }
+        return;
+    }
+    int q = rank + y - V + 2;  // this slice's peer
     if (q >= N) q -= N;
     Codes pc[V];
     float ps[V];
-    float d[W];
-    if (y == 0) {
-        Codes c[V][N];
-        float s[V][N];
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const size_t own = (size_t)rank * C + (L + k * H) * W;
-#pragma unroll
-            for (int p = 0; p < N; ++p) {
-                c[k][p] = load_codes<W, true>(in.codes[p] + own);
-                s[k][p] = in.scales[p][own / kBlock];
-            }
-        }
-        if constexpr (N > 1) {
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const size_t i = (L + k * H) * W;
-                pc[k] = load_codes<W, true>(peers.codes[q] + i);
-                ps[k] = peers.scales[q][i / kBlock];
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const size_t i = (L + k * H) * W;
-            const size_t own = (size_t)rank * C + i;
-            float acc[W];
-            dequant_lane(c[k][0], s[k][0], acc);
-#pragma unroll
-            for (int p = 1; p < N; ++p) {
-                dequant_lane(c[k][p], s[k][p], d);
-#pragma unroll
-                for (int j = 0; j < W; ++j) acc[j] = acc[j] + d[j];
-            }
-            float sc;
-            const Codes code = quantize_lane(acc, &sc);
-            store_codes<W>(cc + i, code);
-            if ((threadIdx.x & (kBlock / W - 1)) == 0) cs[i / kBlock] = sc;
-            dequant_lane(code, sc, d);  // own chunk straight from registers
-            store_lane_nt(out + own, d);
-        }
-        if constexpr (N == 1) return;
-    } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const size_t i = (L + k * H) * W;
-            pc[k] = load_codes<W, true>(peers.codes[q] + i);
-            ps[k] = peers.scales[q][i / kBlock];
-        }
+    for (int k = 0; k < V; ++k) {
+        const size_t i = (t + k * H) * W;
+        pc[k] = load_codes<W, true>(peers.codes[q] + i);
+        ps[k] = peers.scales[q][i / kBlock];
     }
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const size_t i = (L + k * H) * W;
+        const size_t i = (t + k * H) * W;
         dequant_lane(pc[k], ps[k], d);
         store_lane_nt(out + (size_t)q * C + i, d);
     }
 }
 
 // Lane vectors per lane of the fused launch: 2 for fp32 output when one per lane would take more
-// than one round of wavefronts and the slice splits into two halves of whole blocks (C % 256 == 0),
+// than one round of wavefronts and the chunk splits into two halves of whole blocks (C % 256 == 0),
 // else 1.
 static int fused_vectors(int nranks, size_t C, int out_bf16) {
     if (out_bf16 || C % (2 * kBlock) != 0) return 1;
-    const size_t wgs = (C / lane_width<float>() + kThreads - 1) / kThreads * fused_slices(nranks);
+    const size_t wgs = (C / lane_width<float>() + kThreads - 1) / kThreads * fused_slices(nranks, 1);
     return wgs * (kThreads / 64) > kRoundWaves ? 2 : 1;
 }
 
@@ -402,7 +399,7 @@ template <int N, typename Out, int V>
 static hipError_t launch_fused_v(const RankCodes& in, const RankCodes& peers, int rank, size_t C, uint8_t* cc,
                                  float* cs, void* out, hipStream_t stream) {
     const size_t H = C / lane_width<Out>() / V;
-    const dim3 grid((unsigned)((H + kThreads - 1) / kThreads), fused_slices(N));
+    const dim3 grid((unsigned)((H + kThreads - 1) / kThreads), fused_slices(N, V));
     return launch(rs_ag_fused_kernel<N, Out, V>, grid, dim3(kThreads), 0, stream, in, peers, rank, C, H, cc, cs,
                   static_cast<Out*>(out));
 }
