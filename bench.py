@@ -120,9 +120,14 @@ def dda_bytes(n: int, N: int) -> int:
     return (N + 1) * n * 2
 
 
+COPIES_CAP = 0                            # --sets: at most this many copies of every cycle (0: none)
+
+
 def cold_copies(read_bytes: int) -> int:
-    """Buffer copies to cycle so that COLD_READ_BYTES are read between two reads of one copy."""
-    return max(2, -(-COLD_READ_BYTES // read_bytes) + 1)
+    """Buffer copies to cycle so that COLD_READ_BYTES are read between two reads of one copy
+    (at most COPIES_CAP when that is set)."""
+    c = max(2, -(-COLD_READ_BYTES // read_bytes) + 1)
+    return min(c, COPIES_CAP) if COPIES_CAP > 0 else c
 
 
 def fused_grid(n: int, N: int, out_size: int):
@@ -344,6 +349,41 @@ def fused_set(torch, dev, n: int, N: int, out_dtype):
     return b
 
 
+STREAM_GRIDS = (0, 1, 2, 4)      # lpc_measure_stream per_lane: one round, or 1, 2, 4 vectors per lane
+
+
+def stream_ceiling(torch, dev, timer, read_bytes: int, write_bytes: int, batches: int, count: int, warm: int,
+                   kernel: dict = None) -> dict:
+    """The plain streaming kernel (lpc_measure_stream) at a kernel's read and write bytes, cycling
+    cold copies of its source and destination, timed like the kernel at each grid of STREAM_GRIDS;
+    the fastest is the ceiling.  With `kernel` (that kernel's timing) the kernel's line gets
+    ceiling_us, ceiling_gbps and frac_of_ceiling."""
+    from fp8_precision_allreduce_amd import lpc
+
+    copies = cold_copies(read_bytes)
+    src = [torch.ones(read_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    dst = [torch.empty(max(write_bytes, 16), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    best, grids = None, {}
+    for k in STREAM_GRIDS:
+        d = timer.measure(lambda i: lpc.lpc_measure_stream(src[i % copies], read_bytes, dst[i % copies],
+                                                           write_bytes, k),
+                          batches, count, warm, read_bytes + write_bytes)
+        grids["one_round" if k == 0 else "%d_per_lane" % k] = d["us"]
+        if best is None or d["us"] < best["us"]:
+            best = dict(d, grid="one_round" if k == 0 else "%d_per_lane" % k)
+    best["grids_us"] = grids
+    best["copies"] = copies
+    del src, dst
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if kernel is not None:
+        kernel["ceiling_us"] = best["us"]
+        kernel["ceiling_gbps"] = best["gbps"]
+        kernel["ceiling_grid"] = best["grid"]
+        kernel["frac_of_ceiling"] = round(best["us"] / kernel["us"], 4)
+    return best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,7 +393,8 @@ def main():
     ap.add_argument("--launches", type=int, default=100, help="timed launches per batch (the pages' 100)")
     ap.add_argument("--batch-warmup", type=int, default=10, help="untimed launches before each batch (the pages' 10)")
     ap.add_argument("--sets", type=int, default=0,
-                    help="buffer copies of the 16 MiB workload cycled through (0: enough for cold HBM)")
+                    help="at most this many buffer copies in every cycle (0: enough for cold HBM; a small "
+                         "number shortens counter runs, whose byte counts do not depend on it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true",
@@ -362,6 +403,8 @@ def main():
                     help="also run a plain 64 MiB device copy (calibration for counter runs)")
     args = ap.parse_args()
 
+    global COPIES_CAP
+    COPIES_CAP = max(0, args.sets)
     if args.gpus != 1:
         print("bench.py: this benchmark runs on one GPU only (the N ranks are emulated as N buffers "
               "in one GPU's HBM); --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -401,8 +444,8 @@ def main():
 
     # fused-launch sets (only what the fused launch touches) and quantize sets, each cycled
     # every kernel that uses the fused sets reads at least one chunk of every rank (N x 528 KiB)
-    S = args.sets if args.sets > 0 else cold_copies(N * chunk_bytes(C))
-    SQ = args.sets if args.sets > 0 else cold_copies(n * 4)
+    S = cold_copies(N * chunk_bytes(C))
+    SQ = cold_copies(n * 4)
     sets = []
     for _ in range(S):
         b = fused_set(torch, dev, n, N, f32)
@@ -519,16 +562,8 @@ def main():
     # empty launch of each kernel's shape, and a minimal empty launch
     fr, fw = fused_read_bytes(n, N), fused_write_bytes(n, N, 4)
     qr, qw = n * 4, n + n // BLOCK * 4
-    SP = cold_copies(min(fr, qr))
-    pool_src = [torch.ones(max(fr, qr), dtype=u8, device=dev) for _ in range(SP)]
-    pool_dst = [torch.empty(max(fw, qw), dtype=u8, device=dev) for _ in range(SP)]
-
-    def stream(rb, wb):
-        def f(i):
-            lpc.lpc_measure_stream(pool_src[i % SP], rb, pool_dst[i % SP], wb)
-        return f
-    ceil_f = timer.measure(stream(fr, fw), B, L, WB, fr + fw)
-    ceil_q = timer.measure(stream(qr, qw), B, L, WB, qr + qw)
+    ceil_f = stream_ceiling(torch, dev, timer, fr, fw, B, L, WB)
+    ceil_q = stream_ceiling(torch, dev, timer, qr, qw, B, L, WB)
     fgrid = fused_grid(n, N, 4)
     qgrid = (-(-n // (16 * THREADS)), 1)
     floor_f = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_KERNARG, sink),
@@ -540,13 +575,13 @@ def main():
                                ("quantize_f32_16MiB", ceil_q, floor_q, qgrid, QUANT_KERNARG)):
         kernels[k]["ceiling_us"] = c["us"]
         kernels[k]["ceiling_gbps"] = c["gbps"]
+        kernels[k]["ceiling_grid"] = c["grid"]
         kernels[k]["frac_of_ceiling"] = round(c["us"] / kernels[k]["us"], 4)
         kernels[k]["floor_us"] = fl["us"]
         kernels[k]["floor_shape"] = "%dx%d workgroups of %d lanes, %d argument bytes" % (grid[0], grid[1], THREADS, ka)
     kernels["stream_ceiling_fused_mix"] = ceil_f
     kernels["stream_ceiling_quantize_mix"] = ceil_q
     kernels["empty_launch_min"] = empty
-    del pool_src, pool_dst
 
     dda_res = {}
     for T in inputs.DDA_TOKENS:
@@ -664,6 +699,9 @@ def main():
         del sets4, b4
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+        stream_ceiling(torch, dev, timer, fused_read_bytes(n4, N), fused_write_bytes(n4, N, 2), 3, 20, 2,
+                       kernels["rs_ag_fused_bf16_256MiB"])
+        stream_ceiling(torch, dev, timer, n4 * 2, n4 + n4 // BLOCK * 4, 3, 20, 2, kernels["quantize_bf16_256MiB"])
 
         # The fused kernel against message size: fp32, N=8, values as in the 16 MiB workload.  The
         # launch's fixed cost weighs less as the message grows.  Copies cycled for cold HBM.
@@ -696,12 +734,14 @@ def main():
             d = timer.measure(fused_s, 3, L, WB, fused_bytes(ns, N, 4))
             d["frac"] = round(d["gbps"] / HBM_PEAK_GBPS, 4)
             d["copies"] = copies
+            d["grid"] = list(fused_grid(ns, N, 4))
             sizes["%dMiB" % mib] = d
             for b in sets_s[:3 * (WB + L)]:                      # the copies the timed batches used
                 assert torch.equal(b["oc"], sets_s[0]["cc"][0]), "fused %d MiB: reduced chunk differs" % mib
             del sets_s, b_s, fused_s
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
+            stream_ceiling(torch, dev, timer, fused_read_bytes(ns, N), fused_write_bytes(ns, N, 4), 3, L, WB, d)
         kernels["rs_ag_fused_f32_by_size"] = sizes
 
         rows, row_len = inputs.A2AV_ROWS, inputs.A2AV_ROW_LEN
@@ -738,6 +778,9 @@ def main():
         del sets5, b5, a5
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+        stream_ceiling(torch, dev, timer, m5 * 2 + rows * 4, m5 + m5 // BLOCK * 4, 3, 20, 2,
+                       kernels["a2av_quantize_rows_bf16"])
+        stream_ceiling(torch, dev, timer, m5 + m5 // BLOCK * 4, m5 * 2, 3, 20, 2, kernels["a2av_dequantize_bf16"])
 
     if args.copy_probe:
         # a plain copy of known size (64 MiB read, 64 MiB written): the counter calibration
@@ -792,7 +835,8 @@ def main():
             "launches": B * L,
             # the same run's references: a plain kernel with the same bytes and read:write mix, an empty
             # launch of the fused kernel's shape, and a minimal empty launch
-            "ceiling_kernel": "lpc_measure_stream, %d B read + %d B written" % (fr, fw),
+            "ceiling_kernel": "lpc_measure_stream, %d B read + %d B written, fastest of its grids (%s)" % (
+                fr, fw, ceil_f["grid"]),
             "ceiling_us": ceil_f["us"],
             "ceiling_gbps": ceil_f["gbps"],
             "frac_of_ceiling": hk["frac_of_ceiling"],

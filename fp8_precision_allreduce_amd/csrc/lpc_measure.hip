@@ -66,12 +66,14 @@ hipError_t launch_stream(const void* src, size_t nr, void* dst, size_t nw, unsig
 // Per-lane counts are rounded up to 1, 2, 4 or 8 (0 when there is nothing to move).
 int bucket(size_t k) { return k == 0 ? 0 : k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8; }
 
-// Workgroups of the streaming kernel: one round of resident wavefronts (2,048 workgroups of 256
-// lanes, 8 wavefronts per SIMD on 256 CUs) when that leaves at most 8 vectors per lane each way,
-// fewer when there is less to move, more (8 vectors per lane) for larger transfers.
-size_t stream_workgroups(size_t nr, size_t nw) {
+// Workgroups of the streaming kernel.  per_lane == 0: one round of resident wavefronts (2,048
+// workgroups of 256 lanes, 8 wavefronts per SIMD on 256 CUs) when that leaves at most 8 vectors per
+// lane each way, fewer when there is less to move, more (8 vectors per lane) for larger transfers.
+// per_lane == K: as many workgroups as K vectors per lane each way need.
+size_t stream_workgroups(size_t nr, size_t nw, int per_lane) {
     constexpr size_t kRound = 2048, kMaxPerLane = 8;
     const size_t m = std::max(nr, nw);
+    if (per_lane > 0) return (m + kThreads * per_lane - 1) / (kThreads * per_lane);
     const size_t need = (m + kThreads - 1) / kThreads;
     if (need <= kRound) return need;
     if (m <= kRound * kThreads * kMaxPerLane) return kRound;
@@ -110,15 +112,16 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 extern "C" {
 
-lpc_status lpc_measure_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+lpc_status lpc_measure_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, int per_lane,
                               hipStream_t stream) {
     if (read_bytes % 16 || write_bytes % 16) return LPC_ERR_SHAPE;
+    if (per_lane != 0 && per_lane != 1 && per_lane != 2 && per_lane != 4 && per_lane != 8) return LPC_ERR_SHAPE;
     if (read_bytes == 0 && write_bytes == 0) return LPC_OK;
     if ((read_bytes && !src) || !dst) return LPC_ERR_NULL;
     if ((read_bytes && misaligned(src)) || misaligned(dst)) return LPC_ERR_ALIGN;
     int* sink = static_cast<int*>(dst);  // read only: never written
     const size_t nr = read_bytes / 16, nw = write_bytes / 16;
-    const size_t wgs = stream_workgroups(nr, nw);
+    const size_t wgs = stream_workgroups(nr, nw, per_lane);
     if (wgs > (size_t)INT32_MAX / kThreads) return LPC_ERR_SHAPE;
     const size_t L = wgs * kThreads;
     const int kr = bucket((nr + L - 1) / L), kw = bucket((nw + L - 1) / L);

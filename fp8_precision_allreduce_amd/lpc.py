@@ -62,7 +62,7 @@ SIGNATURES = {
     "lpc_allreduce_emulated": [_pp, _int, _sz, _int, _int, _vp, _sz, _vp],
     "lpc_allreduce_emulated_noalloc": [_pp, _int, _sz, _int, _int, _vp],
     # reference kernels for measurement (include/lpc_measure.h)
-    "lpc_measure_stream": [_vp, _sz, _vp, _sz, _vp],
+    "lpc_measure_stream": [_vp, _sz, _vp, _sz, _int, _vp],
     "lpc_measure_empty": [ctypes.c_uint, ctypes.c_uint, ctypes.c_uint, _sz, _vp, _vp],
 }
 
@@ -285,15 +285,16 @@ def lpc_allreduce_emulated_noalloc(bufs, algo: int, stream=None):
           _stream(stream))
 
 
-def lpc_measure_stream(src, read_bytes: int, dst, write_bytes: int, stream=None):
+def lpc_measure_stream(src, read_bytes: int, dst, write_bytes: int, per_lane: int = 0, stream=None):
     """Plain streaming kernel (measurement reference): reads read_bytes of src, writes write_bytes
-    of dst (with write_bytes == 0, dst is a never-written sink of at least 16 bytes)."""
+    of dst (with write_bytes == 0, dst is a never-written sink of at least 16 bytes); per_lane 0
+    is one round of resident wavefronts, 1/2/4/8 that many vectors per lane."""
     if src is not None and src.numel() * src.element_size() < read_bytes:
         raise ValueError("src holds fewer than %d bytes" % read_bytes)
     if dst is not None and dst.numel() * dst.element_size() < max(write_bytes, 16 if read_bytes else 0):
         raise ValueError("dst holds fewer than %d bytes" % max(write_bytes, 16))
     _call("lpc_measure_stream", _dev(src, "src") if src is not None else None, read_bytes,
-          _dev(dst, "dst") if dst is not None else None, write_bytes, _stream(stream))
+          _dev(dst, "dst") if dst is not None else None, write_bytes, per_lane, _stream(stream))
 
 
 def lpc_measure_empty(grid_x: int, grid_y: int, threads: int, kernarg_bytes: int, sink, stream=None):

@@ -31,18 +31,22 @@ extern "C" {
  * to dst (the written values depend on the read ones; their content is
  * otherwise unspecified).  16-byte non-temporal loads and stores, every
  * wavefront instruction covering one contiguous KiB, tiles in the XCD-aware
- * order of the library's kernels.  The grid is one round of resident
- * wavefronts (2,048 workgroups of 256 lanes) or fewer; a lane makes up to 8
- * loads, then up to 8 stores, at a stride of the grid's lane count (larger
- * transfers take more workgroups at 8 per lane).  Measured on cold HBM this
- * was the fastest of the grid sizes and load kinds tried.
+ * order of the library's kernels.  A lane makes up to K loads, then up to K
+ * stores, at a stride of the grid's lane count.  No single grid is fastest
+ * for every size on cold HBM, so the grid is a parameter:
+ *   per_lane == 0: one round of resident wavefronts (2,048 workgroups of 256
+ *     lanes) or fewer, K <= 8 (larger transfers: more workgroups, K = 8);
+ *     fastest of those tried up to tens of MB;
+ *   per_lane == 1, 2, 4 or 8: K = per_lane and as many workgroups as that
+ *     needs; one of these was fastest at hundreds of MB.
  *   src  [read_bytes], device, 16-byte aligned (may be NULL if read_bytes is 0)
  *   dst  [write_bytes], device, 16-byte aligned, must not overlap src.  With
  *        write_bytes == 0 it must still point to 16 valid bytes, which are not
  *        written (the kernel's store to it sits under a flag that is always off,
  *        which keeps the loads live)
- *   read_bytes, write_bytes  multiples of 16 (else LPC_ERR_SHAPE); both 0 is a no-op */
-lpc_status lpc_measure_stream(const void *src, size_t read_bytes, void *dst, size_t write_bytes,
+ *   read_bytes, write_bytes  multiples of 16; per_lane one of 0, 1, 2, 4, 8
+ *        (else LPC_ERR_SHAPE); both sizes 0 is a no-op */
+lpc_status lpc_measure_stream(const void *src, size_t read_bytes, void *dst, size_t write_bytes, int per_lane,
                               hipStream_t stream);
 
 /* Empty launch: grid_x x grid_y workgroups of `threads` lanes whose kernel

@@ -61,15 +61,18 @@ def test_exports_every_declared_function(L):
 
 def test_measure_errors(L):
     s, e = L.lpc_measure_stream, L.lpc_measure_empty
-    assert s(A, 16, A, 16 * 3 + 8, None) == SHAPE
-    assert s(A, 20, A, 16, None) == SHAPE
-    assert s(None, 0, None, 0, None) == OK
-    assert s(None, 16, A, 16, None) == NULL
-    assert s(A, 16, None, 16, None) == NULL
-    assert s(A, 16, None, 0, None) == NULL                 # read only: dst is the sink
-    assert s(B, 16, A, 16, None) == ALIGN
-    assert s(A, 16, B, 16, None) == ALIGN
-    assert s(A, 16, A + 1024, 32, None) == HIP            # passes the checks; no device
+    assert s(A, 16, A, 16 * 3 + 8, 0, None) == SHAPE
+    assert s(A, 20, A, 16, 0, None) == SHAPE
+    for bad in (-1, 3, 5, 16):
+        assert s(A, 16, A + 1024, 16, bad, None) == SHAPE
+    assert s(None, 0, None, 0, 0, None) == OK
+    assert s(None, 16, A, 16, 0, None) == NULL
+    assert s(A, 16, None, 16, 0, None) == NULL
+    assert s(A, 16, None, 0, 0, None) == NULL              # read only: dst is the sink
+    assert s(B, 16, A, 16, 0, None) == ALIGN
+    assert s(A, 16, B, 16, 0, None) == ALIGN
+    for k in (0, 1, 2, 4, 8):
+        assert s(A, 16, A + 1024, 32, k, None) == HIP      # passes the checks; no device
     assert e(0, 1, 64, 8, A, None) == SHAPE
     assert e(1, 0, 64, 8, A, None) == SHAPE
     assert e(1, 1, 0, 8, A, None) == SHAPE
