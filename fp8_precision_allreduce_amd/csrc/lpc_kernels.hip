@@ -424,56 +424,94 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
 // ---------------------------------------------------------------------------
 // DDA flat: N bf16 buffers -> FP32 rank-order sum -> bf16.  Small messages
 // are latency-bound, so the launch spreads them thin: one lane owns 4 bf16
-// (one 8-byte load per rank), 64-lane workgroups; the last partial quad goes
-// element by element.
+// (one 8-byte non-temporal load per rank), 64-lane workgroups.  The last
+// n % 4 elements, if any, go to a second, one-wavefront launch.  Keeping the
+// element-by-element tail out of the main kernel keeps its code small: on
+// cold HBM at 16 KiB per rank the main launch measured 2.07 us against 2.33 us
+// with the tail loop inside (308 against 108 instructions); non-temporal
+// loads measured 2.29 against 2.39 us at 64 KiB.
 // ---------------------------------------------------------------------------
 
 constexpr int kDdaThreads = 64;
 constexpr int kDdaElems = 4;
 
+// the rank-order sum of elements e .. e+3, written as bf16 (loads: NT = non-temporal)
+template <int N, bool NT>
+__device__ __forceinline__ void dda_flat_quad(const RankBufs& b, size_t e, uint16_t* __restrict__ out) {
+    u32x2_t v[N];
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+        const u32x2_t* src = reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(b.p[p]) + e);
+        if constexpr (NT) v[p] = __builtin_nontemporal_load(src);
+        else v[p] = *src;
+    }
+    float acc[kDdaElems] = {bf16lo(v[0][0]), bf16hi(v[0][0]), bf16lo(v[0][1]), bf16hi(v[0][1])};
+#pragma unroll
+    for (int p = 1; p < N; ++p) {
+        acc[0] = acc[0] + bf16lo(v[p][0]);
+        acc[1] = acc[1] + bf16hi(v[p][0]);
+        acc[2] = acc[2] + bf16lo(v[p][1]);
+        acc[3] = acc[3] + bf16hi(v[p][1]);
+    }
+    *reinterpret_cast<uint2*>(out + e) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+}
+
+// the rank-order sum of element i alone
+template <int N>
+__device__ __forceinline__ void dda_flat_one(const RankBufs& b, size_t i, uint16_t* __restrict__ out) {
+    float acc = __uint_as_float((uint32_t)static_cast<const uint16_t*>(b.p[0])[i] << 16);
+#pragma unroll
+    for (int p = 1; p < N; ++p) acc = acc + __uint_as_float((uint32_t)static_cast<const uint16_t*>(b.p[p])[i] << 16);
+    const __bf16 h = (__bf16)acc;
+    out[i] = __builtin_bit_cast(uint16_t, h);
+}
+
 // this lane's elements e .. e+3 (fewer at the tail) of the flat reduce
 template <int N>
 __device__ __forceinline__ void dda_flat_at(const RankBufs& b, size_t n, size_t e, uint16_t* __restrict__ out) {
     if (e + kDdaElems <= n) {
-        uint2 v[N];
-#pragma unroll
-        for (int p = 0; p < N; ++p) v[p] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(b.p[p]) + e);
-        float acc[kDdaElems] = {bf16lo(v[0].x), bf16hi(v[0].x), bf16lo(v[0].y), bf16hi(v[0].y)};
-#pragma unroll
-        for (int p = 1; p < N; ++p) {
-            acc[0] = acc[0] + bf16lo(v[p].x);
-            acc[1] = acc[1] + bf16hi(v[p].x);
-            acc[2] = acc[2] + bf16lo(v[p].y);
-            acc[3] = acc[3] + bf16hi(v[p].y);
-        }
-        *reinterpret_cast<uint2*>(out + e) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        dda_flat_quad<N, false>(b, e, out);
     } else {
-        for (size_t i = e; i < n; ++i) {
-            float acc = __uint_as_float((uint32_t)static_cast<const uint16_t*>(b.p[0])[i] << 16);
-#pragma unroll
-            for (int p = 1; p < N; ++p)
-                acc = acc + __uint_as_float((uint32_t)static_cast<const uint16_t*>(b.p[p])[i] << 16);
-            const __bf16 h = (__bf16)acc;
-            out[i] = __builtin_bit_cast(uint16_t, h);
-        }
+        for (size_t i = e; i < n; ++i) dda_flat_one<N>(b, i, out);
     }
 }
 
+// lanes over the nq = n / 4 whole quads
 template <int N>
-__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t n,
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t nq,
                                                                uint16_t* __restrict__ out) {
-    const size_t e = ((size_t)blockIdx.x * kDdaThreads + threadIdx.x) * kDdaElems;
-    if (e >= n) return;
-    dda_flat_at<N>(b, n, e, out);
+    const size_t q = (size_t)blockIdx.x * kDdaThreads + threadIdx.x;
+    if (q >= nq) return;
+    dda_flat_quad<N, true>(b, q * kDdaElems, out);
+}
+
+// one lane per element of [e0, n) (at most 3)
+template <int N>
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_tail_kernel(RankBufs b, size_t e0, size_t n,
+                                                                    uint16_t* __restrict__ out) {
+    const size_t i = e0 + threadIdx.x;
+    if (i >= n) return;
+    dda_flat_one<N>(b, i, out);
+}
+
+template <int N>
+static hipError_t launch_dda_flat_n(const RankBufs& b, size_t n, uint16_t* out, hipStream_t stream) {
+    const size_t nq = n / kDdaElems;
+    if (nq > 0) {
+        const dim3 grid((unsigned)((nq + kDdaThreads - 1) / kDdaThreads));
+        const hipError_t e = launch(dda_flat_kernel<N>, grid, dim3(kDdaThreads), 0, stream, b, nq, out);
+        if (e != hipSuccess) return e;
+    }
+    if (n % kDdaElems)
+        return launch(dda_flat_tail_kernel<N>, dim3(1), dim3(kDdaThreads), 0, stream, b, nq * kDdaElems, n, out);
+    return hipSuccess;
 }
 
 hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, hipStream_t stream) {
-    const size_t lanes = (n + kDdaElems - 1) / kDdaElems;
-    const dim3 grid((unsigned)((lanes + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
     uint16_t* o = static_cast<uint16_t*>(out);
     switch (nranks) {
 #define LPC_DDA_CASE(NR) \
-    case NR: return launch(dda_flat_kernel<NR>, grid, block, 0, stream, b, n, o);
+    case NR: return launch_dda_flat_n<NR>(b, n, o, stream);
         LPC_DDA_CASE(1) LPC_DDA_CASE(2) LPC_DDA_CASE(3) LPC_DDA_CASE(4)
         LPC_DDA_CASE(5) LPC_DDA_CASE(6) LPC_DDA_CASE(7) LPC_DDA_CASE(8)
 #undef LPC_DDA_CASE

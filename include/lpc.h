@@ -44,7 +44,9 @@
  *     dtype (LPC_ERR_DTYPE), 1 <= nranks <= 8 and 0 <= rank < nranks
  *     (LPC_ERR_RANKS), n == 0 (returns LPC_OK, no work), null pointers
  *     (LPC_ERR_NULL), 16-byte alignment of every pointer (LPC_ERR_ALIGN),
- *     shape (LPC_ERR_SHAPE).  A failed kernel launch gives LPC_ERR_HIP.
+ *     shape (LPC_ERR_SHAPE).  A failed kernel launch gives LPC_ERR_HIP; a
+ *     call that makes two launches (dda_flat_reduce with n % 4 != 0, the
+ *     emulated allreduce) may then leave the first one enqueued.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.  The
  *     FP32 rank-order sum of every element must be finite as well (for
  *     example |x| <= FLT_MAX / nranks everywhere): a block whose sum
@@ -182,7 +184,9 @@ lpc_status lpc_reduce_scatter(const uint8_t *const codes[], const float *const s
  * flat): out[i] = bf16_rne(sum over p = 0..nranks-1, in order, of
  * f32(bufs[p][i])), FP32 accumulation.
  *   bufs[p]  [n] bfloat16 input of rank p;  out [n] bfloat16
- *   n        any element count (no block constraint).
+ *   n        any element count (no block constraint).  One launch, or two
+ *            when n % 4 != 0 (the last n % 4 elements go to a one-wavefront
+ *            launch of their own).
  *   `out` must not alias any input (peers read the inputs concurrently).   */
 lpc_status dda_flat_reduce(const void *const bufs[], int nranks, size_t n, void *out,
                            hipStream_t stream);

@@ -661,13 +661,18 @@ def test_dda_flat_message_sizes(dev, orc, tokens):
     assert_same(to_host(out), orc.dda_flat(bufs), "dda flat T=%d" % tokens)
 
 
-@pytest.mark.parametrize("N,n", [(1, 8), (2, 3), (3, 1001), (8, 8 * 977 + 5), (5, 4096 * 3 + 7)])
+@pytest.mark.parametrize("N,n", [(1, 8), (2, 3), (4, 1), (8, 2), (2, 4), (3, 1001), (8, 8 * 977 + 5),
+                                 (5, 4096 * 3 + 7), (8, 64 * 4 + 3)])
 def test_dda_flat_ragged(dev, orc, N, n):
+    """Element counts with and without a tail of n % 4 elements (the tail goes to a launch of
+    its own), fewer than 4 elements (the tail launch alone), and nothing written past n."""
     bufs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5)) for r in range(N)]
     say("dda flat ragged N=%d n=%d" % (N, n))
-    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    guard = torch.full((n + 64,), -7.0, dtype=torch.bfloat16, device=dev)
+    out = guard[:n]
     lpc.dda_flat_reduce([to_dev(b, dev) for b in bufs], out)
     assert_same(to_host(out), orc.dda_flat(bufs), "dda flat ragged")
+    assert bool((guard[n:] == -7.0).all()), "dda flat wrote past n"
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
