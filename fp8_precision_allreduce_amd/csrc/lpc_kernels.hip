@@ -59,92 +59,111 @@ __device__ __forceinline__ void quantize_at(const In* __restrict__ x, size_t g, 
     if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
 }
 
+// A wavefront quantizes 64 granules (1,024 elements) in one piece: its input, 4 KiB of fp32 or
+// 2 KiB of bf16, comes in with loads that each cover one contiguous KiB (lane l reads bytes
+// 16l..16l+15 of every KiB), non-temporal; LDS then regroups the rows so that each lane holds one
+// whole 16-element granule, and the granule arithmetic follows (one block max and scale per 8
+// lanes).  The non-temporal loads leave no freshly read input in the caches: the launch that
+// follows a quantization (the reduce-scatter) measured about 2 us slower after plain loads at
+// 16 MiB.  Loaded as granules (32 or 64 contiguous bytes a lane), non-temporal loads fetched lines
+// more than once; with ordinary granule loads the bf16 quantizer measured 68.8 us at 256 MiB
+// against 66.9 us regrouped (cold HBM, same run).
+constexpr int kWaveGranules = 64;
+
+// Input rows of one KiB per wavefront (4 fp32, 2 bf16), and 16-byte chunks per granule (as many).
+template <typename In> constexpr uint32_t wave_rows() { return (uint32_t)sizeof(In); }
+
+// LDS byte offset of 16-byte chunk j of granule G within a wavefront's rows: the chunk's slot is
+// rotated by G/4 so that consecutive lanes touch distinct 16-byte bank groups, both when a loaded
+// row is written (4 or 2 lanes per granule) and when a granule is read back (one lane each).
+template <typename In>
+__device__ __forceinline__ uint32_t regroup_slot(uint32_t G, uint32_t j) {
+    constexpr uint32_t R = wave_rows<In>();
+    return G * (16u * R) + (((j + (G >> 2)) & (R - 1)) * 16u);
+}
+
+// Lane l of a wavefront gets granule l of the `left` (64, or fewer, a multiple of 8) granules that
+// start at src, through `lds` (the wavefront's 1 KiB per row).  Lanes l >= left get nothing.
+template <typename In>
+__device__ __forceinline__ void load_wave_granules(const In* __restrict__ src, uint32_t left, uint32_t l,
+                                                   uint8_t* lds, float (&v)[kGranule]) {
+    constexpr uint32_t R = wave_rows<In>();
+    const u32x4_t* rows = reinterpret_cast<const u32x4_t*>(src);
+    u32x4_t r[R];
+    if (left == kWaveGranules) {
+        // every wavefront but possibly the last: all rows in flight at once
+#pragma unroll
+        for (uint32_t k = 0; k < R; ++k) r[k] = __builtin_nontemporal_load(rows + k * 64 + l);
+#pragma unroll
+        for (uint32_t k = 0; k < R; ++k)
+            *reinterpret_cast<u32x4_t*>(lds + regroup_slot<In>(k * (64 / R) + l / R, l % R)) = r[k];
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < R; ++k) {
+            const uint32_t G = k * (64 / R) + l / R;
+            if (G < left) {
+                r[k] = __builtin_nontemporal_load(rows + k * 64 + l);
+                *reinterpret_cast<u32x4_t*>(lds + regroup_slot<In>(G, l % R)) = r[k];
+            }
+        }
+    }
+    // LDS operations of one wavefront complete in order: the reads below see every lane's writes
+    __builtin_amdgcn_wave_barrier();
+    if (l >= left) return;
+#pragma unroll
+    for (uint32_t j = 0; j < R; ++j) {
+        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(lds + regroup_slot<In>(l, j));
+        if constexpr (R == 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[4 * j + q] = __uint_as_float(t[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[8 * j + 2 * q] = bf16lo(t[q]);
+                v[8 * j + 2 * q + 1] = bf16hi(t[q]);
+            }
+        }
+    }
+}
+
+// codes of granule g (non-temporal) and, from the block's first lane, its scale
+__device__ __forceinline__ void store_granule(const uint4& c, float sc, size_t g, uint32_t l,
+                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    const u32x4_t cv = {c.x, c.y, c.z, c.w};
+    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + g * kGranule));
+    if ((l & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = sc;
+}
+
 template <typename In>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const In* __restrict__ x, size_t ngran,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
-    const size_t g = xcd_tile() * kThreads + threadIdx.x;
-    if (g >= ngran) return;  // whole 8-lane groups drop out together (n % 128 == 0)
-    quantize_at(x, g, codes, scales);
-}
-
-// fp32 input.  A wavefront quantizes 64 granules (1,024 elements, 4 KiB of input) with four loads
-// that each cover one contiguous KiB (lane l reads bytes 16l..16l+15 of every KiB), non-temporal;
-// LDS then regroups the four rows so that each lane holds one whole 16-element granule, and the
-// granule arithmetic follows (one block max and scale per 8 lanes).  The non-temporal loads leave
-// no 16 MiB of freshly read input in the caches: the launch that follows a quantization (the
-// reduce-scatter) measured about 2 us slower after plain loads at 16 MiB.  Loaded as granules
-// (64 contiguous bytes a lane), non-temporal loads fetched each line more than once.
-constexpr int kWaveGranules = 64;
-
-// LDS byte offset of 16-byte chunk j of granule G within a wavefront's 4 KiB: the chunk's slot is
-// rotated by G/4 so that 16 consecutive lanes touch 16 distinct 16-byte bank groups, both when a
-// loaded row is written (4 lanes per granule) and when a granule is read back (one lane each).
-__device__ __forceinline__ uint32_t regroup_slot(uint32_t G, uint32_t j) {
-    return G * 64u + (((j + (G >> 2)) & 3u) * 16u);
-}
-
-__global__ __launch_bounds__(kThreads) void quantize_f32_kernel(const float* __restrict__ x, size_t ngran,
-                                                                uint8_t* __restrict__ codes,
-                                                                float* __restrict__ scales) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][kWaveGranules * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][kWaveGranules * 16 * sizeof(In)];
     // the wavefront index read as a wave-uniform value, so that g0, left and the branches on them
     // are scalar
     const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const size_t g0 = (xcd_tile() * (kThreads / 64) + w) * kWaveGranules;
     if (g0 >= ngran) return;  // whole wavefronts past the end
     // granules of this wavefront that exist: all 64, or (the last wavefront) a multiple of 8
-    const size_t left = ngran - g0 < kWaveGranules ? ngran - g0 : kWaveGranules;
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(x + g0 * kGranule);
-    uint8_t* const mine = lds[w];
-    f32x4_t r[4];
-    if (left == kWaveGranules) {
-        // every wavefront but possibly the last: four loads in flight at once
-#pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = __builtin_nontemporal_load(src + k * 64 + l);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<f32x4_t*>(mine + regroup_slot(k * 16 + (l >> 2), l & 3)) = r[k];
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t G = k * 16 + (l >> 2);
-            if (G < left) {
-                r[k] = __builtin_nontemporal_load(src + k * 64 + l);
-                *reinterpret_cast<f32x4_t*>(mine + regroup_slot(G, l & 3)) = r[k];
-            }
-        }
-    }
-    // LDS operations of one wavefront complete in order: the reads below see every lane's writes
-    __builtin_amdgcn_wave_barrier();
-    if (l >= left) return;  // whole 8-lane groups
+    const uint32_t left = (uint32_t)(ngran - g0 < kWaveGranules ? ngran - g0 : kWaveGranules);
     float v[kGranule];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(mine + regroup_slot(l, j));
-        v[4 * j] = t[0];
-        v[4 * j + 1] = t[1];
-        v[4 * j + 2] = t[2];
-        v[4 * j + 3] = t[3];
-    }
+    load_wave_granules(x + g0 * kGranule, left, l, lds[w], v);
+    if (l >= left) return;  // whole 8-lane groups
     float sc;
     const uint4 c = quantize_granule(v, &sc);
-    const size_t g = g0 + l;
-    const u32x4_t cv = {c.x, c.y, c.z, c.w};
-    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + g * kGranule));
-    if ((l & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = sc;
+    store_granule(c, sc, g0 + l, l, codes, scales);
 }
 
 hipError_t launch_quantize(const void* x, int in_bf16, size_t n, uint8_t* codes, float* scales,
                            hipStream_t stream) {
     const size_t ngran = n / kGranule;
-    if (in_bf16)
-        return launch(quantize_kernel<uint16_t>, grid_for(ngran), dim3(kThreads), 0, stream,
-                      static_cast<const uint16_t*>(x), ngran, codes, scales);
     const size_t waves = (ngran + kWaveGranules - 1) / kWaveGranules;
     const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)));
-    return launch(quantize_f32_kernel, grid, dim3(kThreads), 0, stream, static_cast<const float*>(x), ngran, codes,
-                  scales);
+    if (in_bf16)
+        return launch(quantize_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(x),
+                      ngran, codes, scales);
+    return launch(quantize_kernel<float>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(x), ngran,
+                  codes, scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -977,45 +996,76 @@ hipError_t launch_a2av_route(const int32_t* dest, size_t rows, int nranks, int32
 }
 
 // ---------------------------------------------------------------------------
-// gather + quantize rows: flat granules over the packed (row, column) space,
-// in XCD-aware tile order.  A granule never straddles a row (row_len % 128 ==
+// gather + quantize rows: granules over the packed (row, column) space, in
+// XCD-aware tile order.  A granule never straddles a row (row_len % 128 ==
 // 0); its source row is perm[packed row].  An invalid perm entry quantizes a
-// zero row: scale +0, codes 0x00.
+// zero row: scale +0, codes 0x00.  When row_len is a multiple of 1,024, every
+// wavefront's 64 granules lie in one row and come in as one piece, with the
+// quantizer's regrouped non-temporal loads (measured at 16,384 x 7168 bf16,
+// cold HBM); otherwise each lane loads its own granule.
 // ---------------------------------------------------------------------------
 
-template <typename In>
+template <typename In, bool kWave>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const In* __restrict__ x, size_t rows,
                                                                  size_t row_len, const int32_t* __restrict__ perm,
                                                                  uint8_t* __restrict__ codes,
                                                                  float* __restrict__ scales) {
-    const size_t g = xcd_tile() * kThreads + threadIdx.x;  // packed granule index
-    const size_t e = g * kGranule;
-    if (e >= rows * row_len) return;  // whole 8-lane blocks drop out together
-    const size_t k = e / row_len;
-    const size_t col = e - k * row_len;
-    const int32_t src = perm[k];
     float v[kGranule];
-    if (src < 0 || (size_t)src >= rows) {
+    if constexpr (kWave) {
+        __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][kWaveGranules * 16 * sizeof(In)];
+        const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+        const size_t g0 = (xcd_tile() * (kThreads / 64) + w) * kWaveGranules;  // packed granule index
+        const size_t e0 = g0 * kGranule;
+        if (e0 >= rows * row_len) return;  // whole wavefronts (rows * row_len % 1024 == 0)
+        const size_t k = e0 / row_len;     // one packed row for the whole wavefront
+        const int32_t src = perm[k];
+        if (src < 0 || (size_t)src >= rows) {
 #pragma unroll
-        for (int j = 0; j < kGranule; ++j) v[j] = 0.0f;
+            for (int j = 0; j < kGranule; ++j) v[j] = 0.0f;
+        } else {
+            load_wave_granules(x + (size_t)src * row_len + (e0 - k * row_len), kWaveGranules, l, lds[w], v);
+        }
+        float sc;
+        const uint4 c = quantize_granule(v, &sc);
+        store_granule(c, sc, g0 + l, l, codes, scales);
     } else {
-        load16(x + (size_t)src * row_len + col, v);
+        const size_t g = xcd_tile() * kThreads + threadIdx.x;  // packed granule index
+        const size_t e = g * kGranule;
+        if (e >= rows * row_len) return;  // whole 8-lane blocks drop out together
+        const size_t k = e / row_len;
+        const size_t col = e - k * row_len;
+        const int32_t src = perm[k];
+        if (src < 0 || (size_t)src >= rows) {
+#pragma unroll
+            for (int j = 0; j < kGranule; ++j) v[j] = 0.0f;
+        } else {
+            load16(x + (size_t)src * row_len + col, v);
+        }
+        float sc;
+        const uint4 c = quantize_granule(v, &sc);
+        store_granule(c, sc, g, threadIdx.x, codes, scales);
     }
-    float s;
-    const uint4 c = quantize_granule(v, &s);
-    const u32x4_t cv = {c.x, c.y, c.z, c.w};
-    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + e));
-    if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
+}
+
+template <typename In>
+static hipError_t launch_quantize_rows_t(const In* x, size_t rows, size_t row_len, const int32_t* perm,
+                                         uint8_t* codes, float* scales, hipStream_t stream) {
+    const size_t ngran = rows * row_len / kGranule;
+    if (row_len % (kWaveGranules * kGranule) == 0) {
+        const size_t waves = ngran / kWaveGranules;
+        const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)));
+        return launch(quantize_rows_kernel<In, true>, grid, dim3(kThreads), 0, stream, x, rows, row_len, perm, codes,
+                      scales);
+    }
+    return launch(quantize_rows_kernel<In, false>, grid_for(ngran), dim3(kThreads), 0, stream, x, rows, row_len,
+                  perm, codes, scales);
 }
 
 hipError_t launch_quantize_rows(const void* x, int in_bf16, size_t rows, size_t row_len, const int32_t* perm,
                                 uint8_t* codes, float* scales, hipStream_t stream) {
-    const dim3 grid = grid_for(rows * row_len / kGranule), block(kThreads);
     if (in_bf16)
-        return launch(quantize_rows_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(x), rows,
-                      row_len, perm, codes, scales);
-    return launch(quantize_rows_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), rows, row_len,
-                  perm, codes, scales);
+        return launch_quantize_rows_t(static_cast<const uint16_t*>(x), rows, row_len, perm, codes, scales, stream);
+    return launch_quantize_rows_t(static_cast<const float*>(x), rows, row_len, perm, codes, scales, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -957,20 +957,23 @@ def test_a2av_quantize_rows_70000_short_rows(dev, orc):
     assert_same(to_host(scales), rs, "rows scales")
 
 
-def test_a2av_quantize_rows_f32(dev, orc):
-    """Row gather + quantize from fp32 rows (3 blocks per row), with invalid perm entries."""
-    rows, row_len = 257, 384
+@pytest.mark.parametrize("rows,row_len", [(257, 384), (65, 2048)])
+def test_a2av_quantize_rows_f32(dev, orc, rows, row_len):
+    """Row gather + quantize from fp32 rows, with invalid perm entries: 3 blocks per row (each
+    lane loads its own granule) and 16 blocks per row (row_len a multiple of 1,024: every
+    wavefront's granules come in as one piece)."""
     x = inputs.normal_f32(inputs.rng(inputs.A2AV, 3), rows * row_len, 1.0).reshape(rows, row_len)
     _, _, perm = orc.a2av_route(inputs.zipf_destinations(rows=rows), 8)
     p = perm.copy()
-    p[3] = -7
-    p[200] = rows + 5
+    bad = (3, rows - 57)
+    p[bad[0]] = -7
+    p[bad[1]] = rows + 5
     say("a2av quantize rows fp32 rows=%d row_len=%d" % (rows, row_len))
     codes = torch.empty((rows, row_len), dtype=torch.uint8, device=dev)
     scales = torch.empty((rows, row_len // BLOCK), dtype=torch.float32, device=dev)
     lpc.lpc_quantize_fp8_rows(to_dev(x, dev), to_dev(p, dev), codes, scales)
     rc, rs = orc.quantize_rows(x, perm, bf16=False)
-    for k in (3, 200):
+    for k in bad:
         rc[k] = 0
         rs[k] = 0.0
     assert_same(to_host(codes), rc, "fp32 rows codes")
