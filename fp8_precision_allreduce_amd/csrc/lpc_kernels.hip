@@ -46,19 +46,6 @@ static hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t s
 // (1) quantize
 // ---------------------------------------------------------------------------
 
-// quantize granule g of x: codes non-temporal, the block's scale from its first lane
-template <typename In>
-__device__ __forceinline__ void quantize_at(const In* __restrict__ x, size_t g, uint8_t* __restrict__ codes,
-                                            float* __restrict__ scales) {
-    float v[kGranule];
-    load16(x + g * kGranule, v);
-    float s;
-    const uint4 c = quantize_granule(v, &s);
-    const u32x4_t cv = {c.x, c.y, c.z, c.w};
-    __builtin_nontemporal_store(cv, reinterpret_cast<u32x4_t*>(codes + g * kGranule));
-    if ((threadIdx.x & (kLanesPerBlock - 1)) == 0) scales[g / kLanesPerBlock] = s;
-}
-
 // A wavefront quantizes 64 granules (1,024 elements) in one piece: its input, 4 KiB of fp32 or
 // 2 KiB of bf16, comes in with loads that each cover one contiguous KiB (lane l reads bytes
 // 16l..16l+15 of every KiB), non-temporal; LDS then regroups the rows so that each lane holds one
@@ -192,7 +179,7 @@ __device__ __forceinline__ void rank_sum(const RankCodes& in, size_t e, float (&
     float s[N];
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-        c[p] = load_codes<W, false>(in.codes[p] + e);
+        c[p] = load_codes<W, true>(in.codes[p] + e);
         s[p] = in.scales[p][e / kBlock];
     }
     dequant_lane(c[0], s[0], acc);
@@ -268,26 +255,61 @@ hipError_t launch_reduce_scatter_out(const RankCodes& in, int nranks, int rank, 
 // (3) all-gather dequantization (grid.y = chunk);  flat dequantization
 // ---------------------------------------------------------------------------
 
-template <typename Out>
-__global__ __launch_bounds__(kThreads) void allgather_kernel(RankCodes chunks, size_t C,
+// Wavefronts a full MI355X runs at once at 8 per SIMD (256 CUs x 4 SIMDs).
+constexpr size_t kRoundWaves = 8192;
+
+// Lane vectors per lane of a launch whose grid.y has `slices` slices of C / W lane vectors each:
+// 2 (half a slice apart) for fp32 output (W = 4) when one per lane would take more than one round
+// of wavefronts and C splits into two halves of whole blocks (C % 256 == 0), else 1.  On cold HBM
+// a lane's first conversion waits a full load latency, so the launch pays about one latency per
+// round of wavefronts (the all-gather at 16 MiB fp32, N = 8: 5.45 us with one vector per lane,
+// 4.59 us with two).
+static int lane_vectors(size_t slices, size_t C, int W) {
+    if (W != 4 || C % (2 * kBlock) != 0) return 1;
+    const size_t wgs = (C / W + kThreads - 1) / kThreads * slices;
+    return wgs * (kThreads / 64) > kRoundWaves ? 2 : 1;
+}
+
+// chunk p = blockIdx.y; lane t dequantizes vectors t, t + H, ... of it
+template <typename Out, int V>
+__global__ __launch_bounds__(kThreads) void allgather_kernel(RankCodes chunks, size_t C, size_t H,
                                                              Out* __restrict__ out) {
     constexpr int W = lane_width<Out>();
-    const size_t i = lane_elem<W>();
-    if (i >= C) return;
+    using Codes = typename LaneCodes<W>::T;
+    const size_t t = xcd_tile() * kThreads + threadIdx.x;
+    if (t >= H) return;  // whole blocks of 128/W lanes drop out together (H % (128/W) == 0)
     const int p = blockIdx.y;
-    float d[W];
-    dequant_lane(load_codes<W, false>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
-    store_lane_nt(out + (size_t)p * C + i, d);
+    Codes c[V];
+    float s[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const size_t i = (t + k * H) * W;
+        c[k] = load_codes<W, true>(chunks.codes[p] + i);
+        s[k] = chunks.scales[p][i / kBlock];
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const size_t i = (t + k * H) * W;
+        float d[W];
+        dequant_lane(c[k], s[k], d);
+        store_lane_nt(out + (size_t)p * C + i, d);
+    }
+}
+
+template <typename Out, int V>
+static hipError_t launch_allgather_v(const RankCodes& chunks, int nranks, size_t C, void* out, hipStream_t stream) {
+    const size_t H = C / lane_width<Out>() / V;
+    const dim3 grid((unsigned)((H + kThreads - 1) / kThreads), nranks);
+    return launch(allgather_kernel<Out, V>, grid, dim3(kThreads), 0, stream, chunks, C, H, static_cast<Out*>(out));
 }
 
 hipError_t launch_allgather(const RankCodes& chunks, int nranks, size_t n, void* out, int out_bf16,
                             hipStream_t stream) {
     const size_t C = n / nranks;
-    if (out_bf16)
-        return launch(allgather_kernel<uint16_t>, lane_grid<lane_width<uint16_t>()>(C, nranks), dim3(kThreads), 0,
-                      stream, chunks, C, static_cast<uint16_t*>(out));
-    return launch(allgather_kernel<float>, lane_grid<lane_width<float>()>(C, nranks), dim3(kThreads), 0, stream,
-                  chunks, C, static_cast<float*>(out));
+    if (out_bf16) return launch_allgather_v<uint16_t, 1>(chunks, nranks, C, out, stream);
+    if (lane_vectors(nranks, C, lane_width<float>()) == 2)
+        return launch_allgather_v<float, 2>(chunks, nranks, C, out, stream);
+    return launch_allgather_v<float, 1>(chunks, nranks, C, out, stream);
 }
 
 template <typename Out>
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const size_t i = lane_elem<W>();
     if (i >= n) return;
     float d[W];
-    dequant_lane(load_codes<W, false>(codes + i), scales[i / kBlock], d);
+    dequant_lane(load_codes<W, true>(codes + i), scales[i / kBlock], d);
     store_lane_nt(out + i, d);
 }
 
@@ -333,9 +355,6 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, size_t n, v
 // (8 MiB and below) it is faster, and with bf16 output (W = 8) V = 2 measured
 // no faster at 16-256 MiB.
 // ---------------------------------------------------------------------------
-
-// Wavefronts a full MI355X runs at once at 8 per SIMD (256 CUs x 4 SIMDs).
-constexpr size_t kRoundWaves = 8192;
 
 // slices of the fused launch: V reduction slices and one per peer other than rank + 1
 __host__ __device__ constexpr int fused_slices(int N, int V) { return V + (N > 2 ? N - 2 : 0); }
@@ -409,9 +428,8 @@ __global__ __launch_bounds__(kThreads) void rs_ag_fused_kernel(RankCodes in, Ran
 // than one round of wavefronts and the chunk splits into two halves of whole blocks (C % 256 == 0),
 // else 1.
 static int fused_vectors(int nranks, size_t C, int out_bf16) {
-    if (out_bf16 || C % (2 * kBlock) != 0) return 1;
-    const size_t wgs = (C / lane_width<float>() + kThreads - 1) / kThreads * fused_slices(nranks, 1);
-    return wgs * (kThreads / 64) > kRoundWaves ? 2 : 1;
+    if (out_bf16) return 1;
+    return lane_vectors(fused_slices(nranks, 1), C, lane_width<float>());
 }
 
 template <int N, typename Out, int V>
@@ -1099,22 +1117,31 @@ hipError_t launch_encode(const float* x, size_t n, uint8_t* codes, hipStream_t s
 // those of N separate launches, bit for bit, at a third of the launches.
 // ---------------------------------------------------------------------------
 
-// quantize every rank's buffer: grid.y = rank
+// quantize every rank's buffer: grid.y = rank; each wavefront as in quantize_kernel
 template <typename In>
 __global__ __launch_bounds__(kThreads) void quantize_ranks_kernel(RankBufs x, size_t ngran, RankQuant q) {
-    const size_t g = xcd_tile() * kThreads + threadIdx.x;
-    if (g >= ngran) return;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][kWaveGranules * 16 * sizeof(In)];
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const size_t g0 = (xcd_tile() * (kThreads / 64) + w) * kWaveGranules;
+    if (g0 >= ngran) return;
+    const uint32_t left = (uint32_t)(ngran - g0 < kWaveGranules ? ngran - g0 : kWaveGranules);
     const int r = blockIdx.y;
-    quantize_at(static_cast<const In*>(x.p[r]), g, q.codes[r], q.scales[r]);
+    float v[kGranule];
+    load_wave_granules(static_cast<const In*>(x.p[r]) + g0 * kGranule, left, l, lds[w], v);
+    if (l >= left) return;
+    float sc;
+    const uint4 c = quantize_granule(v, &sc);
+    store_granule(c, sc, g0 + l, l, q.codes[r], q.scales[r]);
 }
 
 hipError_t launch_quantize_ranks(const RankBufs& x, int in_bf16, int nranks, size_t n, const RankQuant& q,
                                  hipStream_t stream) {
     const size_t ngran = n / kGranule;
+    const size_t waves = (ngran + kWaveGranules - 1) / kWaveGranules;
+    const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)), nranks);
     if (in_bf16)
-        return launch(quantize_ranks_kernel<uint16_t>, grid_for(ngran, nranks), dim3(kThreads), 0, stream, x,
-                      ngran, q);
-    return launch(quantize_ranks_kernel<float>, grid_for(ngran, nranks), dim3(kThreads), 0, stream, x, ngran, q);
+        return launch(quantize_ranks_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, x, ngran, q);
+    return launch(quantize_ranks_kernel<float>, grid, dim3(kThreads), 0, stream, x, ngran, q);
 }
 
 // reduce-scatter step of every rank: grid.y = the rank owning the chunk
@@ -1154,7 +1181,7 @@ __global__ __launch_bounds__(kThreads) void allgather_ranks_kernel(RankCodes chu
     if (i >= C) return;
     const int p = blockIdx.y, r = blockIdx.z;
     float d[W];
-    dequant_lane(load_codes<W, false>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
+    dequant_lane(load_codes<W, true>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
     store_lane_nt(static_cast<Out*>(outs.p[r]) + (size_t)p * C + i, d);
 }
 

@@ -351,17 +351,18 @@ def test_fused_chunk_sizes(dev, orc, chunk_blocks, bf16):
     compare_allreduce(res, orc.lp_allreduce(xs, bf16=bf16), "chunk_blocks=%d" % chunk_blocks)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 @pytest.mark.parametrize("N,C", [(2, 2097408), (3, 1048832), (5, 524544), (8, 524416)],
                          ids=["N2", "N3", "N5", "N8-odd-blocks"])
-def test_fused_grid_beyond_one_round(dev, orc, N, C):
+def test_fused_grid_beyond_one_round(dev, orc, N, C, fused):
     """Chunks just past the size where one lane vector per lane would take more than
-    one round of wavefronts (8,192): the fp32 fused launch gives each lane two vectors,
-    half a chunk apart (N = 2, 3, 5); with an odd number of blocks per chunk (N = 8) it
-    keeps one.  Every rank's fused launch, every intermediate, in full."""
+    one round of wavefronts (8,192): the fp32 fused and all-gather launches give each lane
+    two vectors, half a chunk apart (N = 2, 3, 5); with an odd number of blocks per chunk
+    (N = 8) they keep one.  Every rank's launches, every intermediate, in full."""
     n = C * N
     xs = [inputs.rank_buffer(inputs.LP_16MIB, r, n) for r in range(N)]
-    say("fused beyond one round: N=%d C=%d n=%d" % (N, C, n))
-    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, True)
+    say("beyond one round: N=%d C=%d n=%d fused=%s" % (N, C, n, fused))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, fused)
     compare_allreduce(res, orc.lp_allreduce(xs), "N=%d C=%d" % (N, C))
 
 
@@ -548,13 +549,20 @@ def test_lp_allreduce_pages_example(dev):
             assert torch.all(out[:n] == N * (N - 1) / 2)
 
 
-def test_lp_allreduce_n8_16MiB_full(dev, orc):
-    """The 16 MiB workload at full size (N=8, 16 MiB fp32 per rank, outliers), every intermediate."""
-    N = 8
-    xs = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(N)]
-    say("lp allreduce 16 MiB full N=8 n=%d" % xs[0].size)
-    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32)
-    compare_allreduce(res, orc.lp_allreduce(xs), "n8 16MiB")
+@pytest.fixture(scope="module")
+def lp_16mib(orc):
+    xs = [inputs.rank_buffer(inputs.LP_16MIB, r) for r in range(8)]
+    return xs, orc.lp_allreduce(xs)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_lp_allreduce_n8_16MiB_full(dev, lp_16mib, fused):
+    """The 16 MiB workload at full size (N=8, 16 MiB fp32 per rank, outliers), every intermediate,
+    through the fused launch and through the reduce-scatter and all-gather launches."""
+    xs, ref = lp_16mib
+    say("lp allreduce 16 MiB full N=8 n=%d fused=%s" % (xs[0].size, fused))
+    res = gpu_lp_allreduce([to_dev(x, dev) for x in xs], torch.float32, fused)
+    compare_allreduce(res, ref, "n8 16MiB")
 
 
 def test_lp_allreduce_n8_256MiB_bf16(dev, orc):
