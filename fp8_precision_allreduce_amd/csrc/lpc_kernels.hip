@@ -1181,7 +1181,9 @@ __global__ __launch_bounds__(kThreads) void allgather_ranks_kernel(RankCodes chu
     if (i >= C) return;
     const int p = blockIdx.y, r = blockIdx.z;
     float d[W];
-    dequant_lane(load_codes<W, true>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
+    // every chunk is read once per rank (grid.z): ordinary loads, so the reads after the first hit
+    // the caches (non-temporal loads measured 26.9 against 22.6 us at N=8 x 16 MiB)
+    dequant_lane(load_codes<W, false>(chunks.codes[p] + i), chunks.scales[p][i / kBlock], d);
     store_lane_nt(static_cast<Out*>(outs.p[r]) + (size_t)p * C + i, d);
 }
 
