@@ -82,6 +82,8 @@ THREADS = 256
 # output pointers
 FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 8 + 3 * 8
 QUANT_KERNARG = 4 * 8                       # x, granule count, codes, scales
+DDA_KERNARG = 8 * 8 + 8 + 8                 # 8 rank pointers, quad count, output
+DDA_THREADS = 64                            # DDA flat workgroup size, one quad (4 elements) a lane
 
 
 # -- algorithmic bytes (every byte read and written, scales included) -------------
@@ -582,12 +584,25 @@ def main():
     kernels["stream_ceiling_fused_mix"] = ceil_f
     kernels["stream_ceiling_quantize_mix"] = ceil_q
     kernels["empty_launch_min"] = empty
+    # the unfused steps against the plain streaming kernel at their own bytes and mix
+    cb = N * chunk_bytes(C)
+    for k, rd, wr in (("reduce_scatter_chunk_16MiB", cb, chunk_bytes(C)),
+                      ("allgather_dequant_f32_16MiB", cb, n * 4),
+                      ("lp_reduce_scatter_f32_16MiB", cb, C * 4)):
+        stream_ceiling(torch, dev, timer, rd, wr, B, L, WB, kernels[k])
 
     dda_res = {}
     for T in inputs.DDA_TOKENS:
         m = dda_host[T][0].size
         r = timer.measure(lambda i, T=T: dda(T, i), B, L, WB, dda_bytes(m, N))
         r["buffer_sets"] = pools[T].shape[0]
+        # the plain streaming kernel at its bytes (8 rank buffers read, one written), and an empty
+        # launch of its grid and argument size
+        stream_ceiling(torch, dev, timer, N * m * 2, m * 2, B, L, WB, r)
+        wgs = -(-m // (4 * DDA_THREADS))
+        r["floor_us"] = timer.measure(lambda i, wgs=wgs: lpc.lpc_measure_empty(wgs, 1, DDA_THREADS, DDA_KERNARG,
+                                                                                sink), B, L, WB)["us"]
+        r["floor_shape"] = "%d workgroups of %d lanes, %d argument bytes" % (wgs, DDA_THREADS, DDA_KERNARG)
         dda_res["%dKiB" % (m * 2 // 1024)] = r
     dda_res["64KiB"]["us_warm"] = timer.measure(lambda i: dda(4, i % 4), B, L, WB)["us"]
     dda_res["64KiB"]["in_step_us"] = step_parts["dda_flat_in_step_us"]
@@ -625,6 +640,8 @@ def main():
     kernels["dda_tree_ag_bf16_2MiB"] = timer.measure(
         lambda i: lpc.dda_tree_allgather(tree_chunks[i % ST], tree_out[i % ST]), B, L, WB, nt * 2 * 2)
     del tree_src, tree_sets, tree_chunks, tree_out
+    stream_ceiling(torch, dev, timer, nt * 2, nt // N * 2, B, L, WB, kernels["dda_tree_rs_bf16_2MiB"])
+    stream_ceiling(torch, dev, timer, nt * 2, nt * 2, B, L, WB, kernels["dda_tree_ag_bf16_2MiB"])
     for algo, name, dt in ((lpc.ALGO_LOW_PRECISION, "low_precision", f32),
                            (lpc.ALGO_DDA_TREE, "dda_tree", f32)):
         ar_bufs = [[torch.empty(n, dtype=dt, device=dev) for _ in range(N)] for _ in range(cold_copies(N * n * 4))]

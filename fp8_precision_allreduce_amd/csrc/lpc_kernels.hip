@@ -460,28 +460,53 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
 
 // ---------------------------------------------------------------------------
 // DDA flat: N bf16 buffers -> FP32 rank-order sum -> bf16.  Small messages
-// are latency-bound, so the launch spreads them thin: one lane owns 4 bf16
-// (one 8-byte non-temporal load per rank), 64-lane workgroups.  The last
-// n % 4 elements, if any, go to a second, one-wavefront launch.  Keeping the
-// element-by-element tail out of the main kernel keeps its code small: on
-// cold HBM at 16 KiB per rank the main launch measured 2.07 us against 2.33 us
-// with the tail loop inside (308 against 108 instructions); non-temporal
-// loads measured 2.29 against 2.39 us at 64 KiB.
+// are latency-bound, so the launch spreads them thin: one lane owns one
+// 32-bit word of every buffer (2 bf16, one 4-byte non-temporal load per
+// rank), 64-lane workgroups in XCD-aware order.  On cold HBM at 64 KiB per
+// rank this measured 2.29 us against 2.38 us with 4 bf16 a lane (8-byte
+// loads) and 2.55-2.62 us with one rank a lane (16-byte loads exchanged
+// through LDS); at 16 KiB 2.17 against 2.32 us.  A last odd element goes to
+// a second, one-wavefront launch, which keeps the element-by-element tail
+// out of the main kernel's code.
+//
+// The same word-wide reduce serves DDA tree's reduce-scatter of one chunk,
+// bf16 or fp32 (2 or 1 elements a lane).
 // ---------------------------------------------------------------------------
 
 constexpr int kDdaThreads = 64;
-constexpr int kDdaElems = 4;
+constexpr int kDdaElems = 4;  // elements a lane of the all-ranks DDA flat launch
 
-// the rank-order sum of elements e .. e+3, written as bf16 (loads: NT = non-temporal)
-template <int N, bool NT>
+// The rank-order FP32 sum of the 32-bit word at byte offset off of every rank's
+// buffer (two bf16, or one fp32), packed back into one word; non-temporal
+// loads, each word is read once.
+template <int N, bool BF16>
+__device__ __forceinline__ uint32_t reduce_word(const RankBufs& b, size_t off) {
+    uint32_t w[N];
+#pragma unroll
+    for (int p = 0; p < N; ++p)
+        w[p] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(b.p[p]) + off));
+    if constexpr (BF16) {
+        float lo = bf16lo(w[0]), hi = bf16hi(w[0]);
+#pragma unroll
+        for (int p = 1; p < N; ++p) {
+            lo = lo + bf16lo(w[p]);
+            hi = hi + bf16hi(w[p]);
+        }
+        return pack_bf16x2(lo, hi);
+    } else {
+        float acc = __uint_as_float(w[0]);
+#pragma unroll
+        for (int p = 1; p < N; ++p) acc = acc + __uint_as_float(w[p]);
+        return __float_as_uint(acc);
+    }
+}
+
+// the rank-order sum of elements e .. e+3, written as bf16 (ordinary loads)
+template <int N>
 __device__ __forceinline__ void dda_flat_quad(const RankBufs& b, size_t e, uint16_t* __restrict__ out) {
     u32x2_t v[N];
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-        const u32x2_t* src = reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(b.p[p]) + e);
-        if constexpr (NT) v[p] = __builtin_nontemporal_load(src);
-        else v[p] = *src;
-    }
+    for (int p = 0; p < N; ++p) v[p] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(b.p[p]) + e);
     float acc[kDdaElems] = {bf16lo(v[0][0]), bf16hi(v[0][0]), bf16lo(v[0][1]), bf16hi(v[0][1])};
 #pragma unroll
     for (int p = 1; p < N; ++p) {
@@ -507,22 +532,21 @@ __device__ __forceinline__ void dda_flat_one(const RankBufs& b, size_t i, uint16
 template <int N>
 __device__ __forceinline__ void dda_flat_at(const RankBufs& b, size_t n, size_t e, uint16_t* __restrict__ out) {
     if (e + kDdaElems <= n) {
-        dda_flat_quad<N, false>(b, e, out);
+        dda_flat_quad<N>(b, e, out);
     } else {
         for (size_t i = e; i < n; ++i) dda_flat_one<N>(b, i, out);
     }
 }
 
-// lanes over the nq = n / 4 whole quads
+// lanes over the nw = n / 2 whole words
 template <int N>
-__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t nq,
-                                                               uint16_t* __restrict__ out) {
-    const size_t q = (size_t)blockIdx.x * kDdaThreads + threadIdx.x;
-    if (q >= nq) return;
-    dda_flat_quad<N, true>(b, q * kDdaElems, out);
+__global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t nw, uint32_t* __restrict__ out) {
+    const size_t w = xcd_tile() * kDdaThreads + threadIdx.x;
+    if (w >= nw) return;
+    out[w] = reduce_word<N, true>(b, w * 4);
 }
 
-// one lane per element of [e0, n) (at most 3)
+// one lane per element of [e0, n) (at most 1)
 template <int N>
 __global__ __launch_bounds__(kDdaThreads) void dda_flat_tail_kernel(RankBufs b, size_t e0, size_t n,
                                                                     uint16_t* __restrict__ out) {
@@ -533,14 +557,14 @@ __global__ __launch_bounds__(kDdaThreads) void dda_flat_tail_kernel(RankBufs b, 
 
 template <int N>
 static hipError_t launch_dda_flat_n(const RankBufs& b, size_t n, uint16_t* out, hipStream_t stream) {
-    const size_t nq = n / kDdaElems;
-    if (nq > 0) {
-        const dim3 grid((unsigned)((nq + kDdaThreads - 1) / kDdaThreads));
-        const hipError_t e = launch(dda_flat_kernel<N>, grid, dim3(kDdaThreads), 0, stream, b, nq, out);
+    const size_t nw = n / 2;
+    if (nw > 0) {
+        const dim3 grid((unsigned)((nw + kDdaThreads - 1) / kDdaThreads));
+        const hipError_t e = launch(dda_flat_kernel<N>, grid, dim3(kDdaThreads), 0, stream, b, nw,
+                                    reinterpret_cast<uint32_t*>(out));
         if (e != hipSuccess) return e;
     }
-    if (n % kDdaElems)
-        return launch(dda_flat_tail_kernel<N>, dim3(1), dim3(kDdaThreads), 0, stream, b, nq * kDdaElems, n, out);
+    if (n % 2) return launch(dda_flat_tail_kernel<N>, dim3(1), dim3(kDdaThreads), 0, stream, b, nw * 2, n, out);
     return hipSuccess;
 }
 
@@ -558,7 +582,8 @@ hipError_t launch_dda_flat(const RankBufs& b, int nranks, size_t n, void* out, h
 
 // ---------------------------------------------------------------------------
 // DDA tree (unquantized): reduce-scatter of one chunk, and the gather copy.
-// Granule = 16 bytes (4 fp32 or 8 bf16).
+// The all-ranks reduce-scatter and the gather copy move 16-byte granules (4
+// fp32 or 8 bf16); the one-rank reduce-scatter moves 32-bit words.
 // ---------------------------------------------------------------------------
 
 // the rank-order sum of the 16-byte granule at byte offset `off` of every
@@ -602,26 +627,30 @@ __device__ __forceinline__ void dda_tree_rs_at(const RankBufs& b, size_t off, vo
     }
 }
 
+// One rank's chunk: one 32-bit word a lane, like DDA flat, in 64-lane workgroups.  At
+// 2 MiB bf16 per rank on cold HBM this measured 2.56 us against 2.95 us for 16-byte
+// granules with ordinary loads in 256-lane workgroups.
 template <int N, bool BF16>
-__global__ __launch_bounds__(kThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes,
-                                                               size_t ngran, void* __restrict__ out) {
-    const size_t g = granule_id();
-    if (g >= ngran) return;
-    dda_tree_rs_at<N, BF16>(b, chunk_off_bytes + g * 16, static_cast<uint4*>(out) + g);
+__global__ __launch_bounds__(kDdaThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes, size_t nw,
+                                                                  uint32_t* __restrict__ out) {
+    const size_t w = (size_t)blockIdx.x * kDdaThreads + threadIdx.x;
+    if (w >= nw) return;
+    out[w] = reduce_word<N, BF16>(b, chunk_off_bytes + w * 4);
 }
 
 hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank, size_t n, void* out,
                               hipStream_t stream) {
     const size_t esz = bf16 ? 2 : 4;
     const size_t chunk_bytes = n / nranks * esz;
-    const size_t ngran = chunk_bytes / 16;
+    const size_t nw = chunk_bytes / 4;
     const size_t off = (size_t)rank * chunk_bytes;
-    const dim3 grid = grid_for(ngran), block(kThreads);
+    uint32_t* o = static_cast<uint32_t*>(out);
+    const dim3 grid((unsigned)((nw + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
     switch (nranks) {
-#define LPC_TREE_CASE(NR)                                                                              \
-    case NR:                                                                                           \
-        if (bf16) return launch(dda_tree_rs_kernel<NR, true>, grid, block, 0, stream, b, off, ngran, out); \
-        return launch(dda_tree_rs_kernel<NR, false>, grid, block, 0, stream, b, off, ngran, out);
+#define LPC_TREE_CASE(NR)                                                                            \
+    case NR:                                                                                         \
+        if (bf16) return launch(dda_tree_rs_kernel<NR, true>, grid, block, 0, stream, b, off, nw, o); \
+        return launch(dda_tree_rs_kernel<NR, false>, grid, block, 0, stream, b, off, nw, o);
         LPC_TREE_CASE(1) LPC_TREE_CASE(2) LPC_TREE_CASE(3) LPC_TREE_CASE(4)
         LPC_TREE_CASE(5) LPC_TREE_CASE(6) LPC_TREE_CASE(7) LPC_TREE_CASE(8)
 #undef LPC_TREE_CASE

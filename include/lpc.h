@@ -45,7 +45,7 @@
  *     (LPC_ERR_RANKS), n == 0 (returns LPC_OK, no work), null pointers
  *     (LPC_ERR_NULL), 16-byte alignment of every pointer (LPC_ERR_ALIGN),
  *     shape (LPC_ERR_SHAPE).  A failed kernel launch gives LPC_ERR_HIP; a
- *     call that makes two launches (dda_flat_reduce with n % 4 != 0, the
+ *     call that makes two launches (dda_flat_reduce with n odd, the
  *     emulated allreduce) may then leave the first one enqueued.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.  The
  *     FP32 rank-order sum of every element must be finite as well (for
@@ -185,8 +185,8 @@ lpc_status lpc_reduce_scatter(const uint8_t *const codes[], const float *const s
  * f32(bufs[p][i])), FP32 accumulation.
  *   bufs[p]  [n] bfloat16 input of rank p;  out [n] bfloat16
  *   n        any element count (no block constraint).  One launch, or two
- *            when n % 4 != 0 (the last n % 4 elements go to a one-wavefront
- *            launch of their own).
+ *            when n is odd (the last element goes to a one-wavefront launch
+ *            of its own).
  *   `out` must not alias any input (peers read the inputs concurrently).   */
 lpc_status dda_flat_reduce(const void *const bufs[], int nranks, size_t n, void *out,
                            hipStream_t stream);

@@ -672,8 +672,8 @@ def test_dda_flat_message_sizes(dev, orc, tokens):
 @pytest.mark.parametrize("N,n", [(1, 8), (2, 3), (4, 1), (8, 2), (2, 4), (3, 1001), (8, 8 * 977 + 5),
                                  (5, 4096 * 3 + 7), (8, 64 * 4 + 3)])
 def test_dda_flat_ragged(dev, orc, N, n):
-    """Element counts with and without a tail of n % 4 elements (the tail goes to a launch of
-    its own), fewer than 4 elements (the tail launch alone), and nothing written past n."""
+    """Even and odd element counts (an odd last element goes to a launch of its own), a single
+    element (the tail launch alone), and nothing written past n."""
     bufs = [inputs.truncate_to_bf16(inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5)) for r in range(N)]
     say("dda flat ragged N=%d n=%d" % (N, n))
     guard = torch.full((n + 64,), -7.0, dtype=torch.bfloat16, device=dev)
@@ -681,6 +681,24 @@ def test_dda_flat_ragged(dev, orc, N, n):
     lpc.dda_flat_reduce([to_dev(b, dev) for b in bufs], out)
     assert_same(to_host(out), orc.dda_flat(bufs), "dda flat ragged")
     assert bool((guard[n:] == -7.0).all()), "dda flat wrote past n"
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N,n", [(8, 8 * 8), (3, 3 * 8 * 77), (5, 5 * 8 * 1001)])
+def test_dda_tree_rs_guarded(dev, orc, bf16, N, n):
+    """One rank's tree reduce-scatter at chunk sizes that leave a partial workgroup, for the
+    first and the last rank, and nothing written past the chunk."""
+    fb = [inputs.normal_f32(inputs.rng(inputs.DDA_FLAT, r), n, 0.5) for r in range(N)]
+    bufs = [inputs.truncate_to_bf16(x) for x in fb] if bf16 else fb
+    dt = torch.bfloat16 if bf16 else torch.float32
+    bd = [to_dev(b, dev) for b in bufs]
+    C = n // N
+    for r in (0, N - 1):
+        say("dda tree rs guarded N=%d n=%d rank %d bf16=%s" % (N, n, r, bf16))
+        guard = torch.full((C + 64,), -7.0, dtype=dt, device=dev)
+        lpc.dda_tree_reduce_scatter(bd, r, guard[:C])
+        assert_same(to_host(guard[:C]), orc.dda_tree_rs(bufs, r, bf16), "dda tree rs %d" % r)
+        assert bool((guard[C:] == -7.0).all()), "dda tree rs wrote past the chunk"
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
