@@ -83,7 +83,7 @@ THREADS = 256
 FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 8 + 3 * 8
 QUANT_KERNARG = 4 * 8                       # x, granule count, codes, scales
 DDA_KERNARG = 8 * 8 + 8 + 8                 # 8 rank pointers, quad count, output
-DDA_THREADS = 64                            # DDA flat workgroup size, one quad (4 elements) a lane
+DDA_THREADS = 64                            # DDA flat workgroup size, one 32-bit word (2 bf16) a lane
 
 
 # -- algorithmic bytes (every byte read and written, scales included) -------------
@@ -599,7 +599,7 @@ def main():
         # the plain streaming kernel at its bytes (8 rank buffers read, one written), and an empty
         # launch of its grid and argument size
         stream_ceiling(torch, dev, timer, N * m * 2, m * 2, B, L, WB, r)
-        wgs = -(-m // (4 * DDA_THREADS))
+        wgs = -(-m // (2 * DDA_THREADS))
         r["floor_us"] = timer.measure(lambda i, wgs=wgs: lpc.lpc_measure_empty(wgs, 1, DDA_THREADS, DDA_KERNARG,
                                                                                 sink), B, L, WB)["us"]
         r["floor_shape"] = "%d workgroups of %d lanes, %d argument bytes" % (wgs, DDA_THREADS, DDA_KERNARG)
