@@ -5,7 +5,9 @@
 // The quantizers use one 16-element granule per lane (a wavefront covers 8
 // scale blocks); the reduce-scatter, all-gather, fused and dequantize kernels
 // give each lane a vector of 4 or 8 elements, so that every lane writes 16
-// bytes (see lpc_device.hpp).  Streaming kernels use 256-lane workgroups.
+// bytes (see lpc_device.hpp); DDA flat and DDA tree's one-rank reduce-scatter
+// give each lane one 32-bit word of every rank's buffer, in 64-lane
+// workgroups.  The other kernels use 256-lane workgroups.
 // Rank loops are unrolled by template parameter so that all N loads of a lane
 // are in flight before the first add.
 #include <tuple>
