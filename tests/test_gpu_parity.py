@@ -447,8 +447,8 @@ def test_fused_at_the_largest_size(dev, orc):
 
 
 def test_graph_replays_match_eager(dev):
-    """The benchmark times HIP graph replays: capture quantize + fused RS+AG + DDA
-    flat, replay it three times with eager work and synchronisation in between,
+    """A caller may capture the step (quantize + fused RS+AG + DDA flat) in a HIP
+    graph: replay it three times with eager work and synchronisation in between,
     and check every replay against the eager result."""
     N = 8
     n = BLOCK * N * 40
