@@ -40,8 +40,8 @@ value = algorithmic bytes of one fused RS+AG launch / its mean duration
 two references timed the same way in the same run: a plain streaming kernel
 moving the same bytes at the same read:write mix (lpc_measure_stream, the
 practical ceiling), and an empty launch of the fused kernel's shape
-(lpc_measure_empty: its grid and argument size, the fixed cost of that
-launch).  traffic is the HBM byte count per launch from rocprofv3 counters
+(lpc_measure_empty: its grid, each wavefront loading about as many argument
+bytes as the fused kernel's do; the fixed cost of that launch).  traffic is the HBM byte count per launch from rocprofv3 counters
 (profiles/traffic.json), null when those counters were taken on other kernel
 sources.  cpu_baseline is the CPU oracle on a bounded sample of the same
 share, on one host core.
@@ -81,6 +81,10 @@ THREADS = 256
 # pointers each), rank, C, the lane stride H, and the chunk-code, chunk-scale and
 # output pointers
 FUSED_KERNARG = 2 * 16 * 8 + 8 + 8 + 8 + 3 * 8
+# argument bytes a fused wavefront loads: a reduction wavefront the 8 ranks' code and scale pointers, one
+# peer's and the scalars (about 170), a peer wavefront one peer's pointers and the scalars (about 56);
+# three of four wavefronts are peer wavefronts
+FUSED_WAVE_ARG_BYTES = 64
 QUANT_KERNARG = 4 * 8                       # x, granule count, codes, scales
 DDA_KERNARG = 8 * 8 + 8 + 8                 # 8 rank pointers, quad count, output
 DDA_THREADS = 64                            # DDA flat workgroup size, one 32-bit word (2 bf16) a lane
@@ -568,19 +572,25 @@ def main():
     ceil_q = stream_ceiling(torch, dev, timer, qr, qw, B, L, WB)
     fgrid = fused_grid(n, N, 4)
     qgrid = (-(-n // (16 * THREADS)), 1)
-    floor_f = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_KERNARG, sink),
-                            B, L, WB)
+    floor_f = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_WAVE_ARG_BYTES,
+                                                            sink), B, L, WB)
+    # the same grid with every wavefront loading all 304 argument bytes: scalar loads of the argument
+    # block cost at this many wavefronts (an upper reference, not the fused launch's behaviour)
+    floor_f_all = timer.measure(lambda i: lpc.lpc_measure_empty(fgrid[0], fgrid[1], THREADS, FUSED_KERNARG, sink),
+                                B, L, WB)
     floor_q = timer.measure(lambda i: lpc.lpc_measure_empty(qgrid[0], qgrid[1], THREADS, QUANT_KERNARG, sink),
                             B, L, WB)
     empty = timer.measure(lambda i: lpc.lpc_measure_empty(1, 1, 64, 16, sink), B, L, WB)
-    for k, c, fl, grid, ka in (("rs_ag_fused_f32_16MiB", ceil_f, floor_f, fgrid, FUSED_KERNARG),
+    for k, c, fl, grid, ka in (("rs_ag_fused_f32_16MiB", ceil_f, floor_f, fgrid, FUSED_WAVE_ARG_BYTES),
                                ("quantize_f32_16MiB", ceil_q, floor_q, qgrid, QUANT_KERNARG)):
         kernels[k]["ceiling_us"] = c["us"]
         kernels[k]["ceiling_gbps"] = c["gbps"]
         kernels[k]["ceiling_grid"] = c["grid"]
         kernels[k]["frac_of_ceiling"] = round(c["us"] / kernels[k]["us"], 4)
         kernels[k]["floor_us"] = fl["us"]
-        kernels[k]["floor_shape"] = "%dx%d workgroups of %d lanes, %d argument bytes" % (grid[0], grid[1], THREADS, ka)
+        kernels[k]["floor_shape"] = "%dx%d workgroups of %d lanes, %d argument bytes loaded a wavefront" % (
+            grid[0], grid[1], THREADS, ka)
+    kernels["rs_ag_fused_f32_16MiB"]["floor_all_args_us"] = floor_f_all["us"]
     kernels["stream_ceiling_fused_mix"] = ceil_f
     kernels["stream_ceiling_quantize_mix"] = ceil_q
     kernels["empty_launch_min"] = empty
@@ -602,7 +612,8 @@ def main():
         wgs = -(-m // (2 * DDA_THREADS))
         r["floor_us"] = timer.measure(lambda i, wgs=wgs: lpc.lpc_measure_empty(wgs, 1, DDA_THREADS, DDA_KERNARG,
                                                                                 sink), B, L, WB)["us"]
-        r["floor_shape"] = "%d workgroups of %d lanes, %d argument bytes" % (wgs, DDA_THREADS, DDA_KERNARG)
+        r["floor_shape"] = "%d workgroups of %d lanes, %d argument bytes loaded a wavefront" % (
+            wgs, DDA_THREADS, DDA_KERNARG)
         dda_res["%dKiB" % (m * 2 // 1024)] = r
     dda_res["64KiB"]["us_warm"] = timer.measure(lambda i: dda(4, i % 4), B, L, WB)["us"]
     dda_res["64KiB"]["in_step_us"] = step_parts["dda_flat_in_step_us"]

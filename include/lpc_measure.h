@@ -52,7 +52,10 @@ lpc_status lpc_measure_stream(const void *src, size_t read_bytes, void *dst, siz
 /* Empty launch: grid_x x grid_y workgroups of `threads` lanes whose kernel
  * argument block is kernarg_bytes rounded up to 16, 64, 128, 256, 320 or 512
  * bytes (plus the grid size the runtime appends).  Every wavefront loads the
- * whole block and writes nothing.
+ * whole block and writes nothing.  At thousands of wavefronts the launch's
+ * time grows with the argument bytes each wavefront loads (the scalar loads'
+ * return bandwidth), so to match a kernel give the bytes one of its
+ * wavefronts loads, not the size of its whole argument block.
  *   grid_x, grid_y >= 1; 1 <= threads <= 1024; kernarg_bytes <= 512 (else LPC_ERR_SHAPE)
  *   sink  a valid device pointer to at least 4 bytes, 16-byte aligned; never written */
 lpc_status lpc_measure_empty(unsigned grid_x, unsigned grid_y, unsigned threads, size_t kernarg_bytes,
