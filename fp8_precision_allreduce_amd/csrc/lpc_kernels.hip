@@ -631,13 +631,17 @@ __device__ __forceinline__ void dda_tree_rs_at(const RankBufs& b, size_t off, vo
 
 // One rank's chunk: one 32-bit word a lane, like DDA flat, in 64-lane workgroups.  At
 // 2 MiB bf16 per rank on cold HBM this measured 2.56 us against 2.95 us for 16-byte
-// granules with ordinary loads in 256-lane workgroups.
+// granules with ordinary loads in 256-lane workgroups.  A chunk of more than 2^31 words
+// (a single fp32 rank of 2^32 elements) would need more lanes than a launch may have:
+// the grid stops at kTreeMaxGroups and its lanes take every grid-size-th word.
+constexpr size_t kTreeMaxGroups = (size_t)1 << 25;
+
 template <int N, bool BF16>
 __global__ __launch_bounds__(kDdaThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes, size_t nw,
                                                                   uint32_t* __restrict__ out) {
-    const size_t w = (size_t)blockIdx.x * kDdaThreads + threadIdx.x;
-    if (w >= nw) return;
-    out[w] = reduce_word<N, BF16>(b, chunk_off_bytes + w * 4);
+    const size_t stride = (size_t)gridDim.x * kDdaThreads;
+    for (size_t w = (size_t)blockIdx.x * kDdaThreads + threadIdx.x; w < nw; w += stride)
+        out[w] = reduce_word<N, BF16>(b, chunk_off_bytes + w * 4);
 }
 
 hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank, size_t n, void* out,
@@ -647,7 +651,8 @@ hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank,
     const size_t nw = chunk_bytes / 4;
     const size_t off = (size_t)rank * chunk_bytes;
     uint32_t* o = static_cast<uint32_t*>(out);
-    const dim3 grid((unsigned)((nw + kDdaThreads - 1) / kDdaThreads)), block(kDdaThreads);
+    const size_t groups = (nw + kDdaThreads - 1) / kDdaThreads;
+    const dim3 grid((unsigned)(groups < kTreeMaxGroups ? groups : kTreeMaxGroups)), block(kDdaThreads);
     switch (nranks) {
 #define LPC_TREE_CASE(NR)                                                                            \
     case NR:                                                                                         \

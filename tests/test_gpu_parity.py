@@ -684,7 +684,7 @@ def test_dda_flat_ragged(dev, orc, N, n):
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-@pytest.mark.parametrize("N,n", [(8, 8 * 8), (3, 3 * 8 * 77), (5, 5 * 8 * 1001)])
+@pytest.mark.parametrize("N,n", [(1, 8 * 37), (2, 2 * 8 * 5), (8, 8 * 8), (3, 3 * 8 * 77), (5, 5 * 8 * 1001)])
 def test_dda_tree_rs_guarded(dev, orc, bf16, N, n):
     """One rank's tree reduce-scatter at chunk sizes that leave a partial workgroup, for the
     first and the last rank, and nothing written past the chunk."""
@@ -699,6 +699,26 @@ def test_dda_tree_rs_guarded(dev, orc, bf16, N, n):
         lpc.dda_tree_reduce_scatter(bd, r, guard[:C])
         assert_same(to_host(guard[:C]), orc.dda_tree_rs(bufs, r, bf16), "dda tree rs %d" % r)
         assert bool((guard[C:] == -7.0).all()), "dda tree rs wrote past the chunk"
+
+
+def test_dda_tree_rs_at_the_largest_size(dev):
+    """One fp32 rank of n = LPC_MAX_ELEMS (16 GiB): a chunk of 2^32 words, more than one launch
+    has lanes for, so the grid's lanes take every grid-size-th word.  With one rank the reduce
+    is the identity; checked on words on both sides of every 1 GiB and 4,096 random ones."""
+    n = lpc.MAX_ELEMS
+    say("dda tree rs at n = %d, N = 1" % n)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(117)
+    x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32)
+    out = torch.zeros(n, dtype=torch.float32, device=dev)
+    lpc.dda_tree_reduce_scatter([x], 0, out)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(117))
+    marks = [0, 1, n - 2, n - 1] + [k * (n // 16) + d for k in range(1, 16) for d in (-1, 0)]
+    idx = torch.from_numpy(np.unique(np.concatenate([np.array(marks), rng.integers(0, n, 4096)]))).to(dev)
+    assert torch.equal(out[idx].view(torch.int32), x[idx].view(torch.int32)), "max-size tree reduce-scatter"
+    del x, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
