@@ -478,6 +478,12 @@ hipError_t launch_rs_ag_fused(const RankCodes& in, const RankCodes& peers, int n
 constexpr int kDdaThreads = 64;
 constexpr int kDdaElems = 4;  // elements a lane of the all-ranks DDA flat launch
 
+// A launch takes at most 2^31 - 1 lanes along a grid dimension.  One word a lane
+// reaches that only for buffers near the largest accepted size (2^32 bf16, or a
+// 2^32-element fp32 chunk); such a launch stops at kMaxWordGroups workgroups and
+// its lanes take every grid-size-th word (the Strided variants below).
+constexpr size_t kMaxWordGroups = ((size_t)1 << 31) / kDdaThreads - 1;
+
 // The rank-order FP32 sum of the 32-bit word at byte offset off of every rank's
 // buffer (two bf16, or one fp32), packed back into one word; non-temporal
 // loads, each word is read once.
@@ -541,11 +547,16 @@ __device__ __forceinline__ void dda_flat_at(const RankBufs& b, size_t n, size_t 
 }
 
 // lanes over the nw = n / 2 whole words
-template <int N>
+template <int N, bool Strided>
 __global__ __launch_bounds__(kDdaThreads) void dda_flat_kernel(RankBufs b, size_t nw, uint32_t* __restrict__ out) {
     const size_t w = xcd_tile() * kDdaThreads + threadIdx.x;
-    if (w >= nw) return;
-    out[w] = reduce_word<N, true>(b, w * 4);
+    if constexpr (Strided) {
+        const size_t stride = (size_t)gridDim.x * kDdaThreads;
+        for (size_t v = w; v < nw; v += stride) out[v] = reduce_word<N, true>(b, v * 4);
+    } else {
+        if (w >= nw) return;
+        out[w] = reduce_word<N, true>(b, w * 4);
+    }
 }
 
 // one lane per element of [e0, n) (at most 1)
@@ -561,9 +572,13 @@ template <int N>
 static hipError_t launch_dda_flat_n(const RankBufs& b, size_t n, uint16_t* out, hipStream_t stream) {
     const size_t nw = n / 2;
     if (nw > 0) {
-        const dim3 grid((unsigned)((nw + kDdaThreads - 1) / kDdaThreads));
-        const hipError_t e = launch(dda_flat_kernel<N>, grid, dim3(kDdaThreads), 0, stream, b, nw,
-                                    reinterpret_cast<uint32_t*>(out));
+        const size_t groups = (nw + kDdaThreads - 1) / kDdaThreads;
+        uint32_t* o = reinterpret_cast<uint32_t*>(out);
+        const hipError_t e =
+            groups <= kMaxWordGroups
+                ? launch(dda_flat_kernel<N, false>, dim3((unsigned)groups), dim3(kDdaThreads), 0, stream, b, nw, o)
+                : launch(dda_flat_kernel<N, true>, dim3((unsigned)kMaxWordGroups), dim3(kDdaThreads), 0, stream, b,
+                         nw, o);
         if (e != hipSuccess) return e;
     }
     if (n % 2) return launch(dda_flat_tail_kernel<N>, dim3(1), dim3(kDdaThreads), 0, stream, b, nw * 2, n, out);
@@ -631,17 +646,28 @@ __device__ __forceinline__ void dda_tree_rs_at(const RankBufs& b, size_t off, vo
 
 // One rank's chunk: one 32-bit word a lane, like DDA flat, in 64-lane workgroups.  At
 // 2 MiB bf16 per rank on cold HBM this measured 2.56 us against 2.95 us for 16-byte
-// granules with ordinary loads in 256-lane workgroups.  A chunk of more than 2^31 words
-// (a single fp32 rank of 2^32 elements) would need more lanes than a launch may have:
-// the grid stops at kTreeMaxGroups and its lanes take every grid-size-th word.
-constexpr size_t kTreeMaxGroups = (size_t)1 << 25;
-
-template <int N, bool BF16>
+// granules with ordinary loads in 256-lane workgroups.
+template <int N, bool BF16, bool Strided>
 __global__ __launch_bounds__(kDdaThreads) void dda_tree_rs_kernel(RankBufs b, size_t chunk_off_bytes, size_t nw,
                                                                   uint32_t* __restrict__ out) {
-    const size_t stride = (size_t)gridDim.x * kDdaThreads;
-    for (size_t w = (size_t)blockIdx.x * kDdaThreads + threadIdx.x; w < nw; w += stride)
+    const size_t w = (size_t)blockIdx.x * kDdaThreads + threadIdx.x;
+    if constexpr (Strided) {
+        const size_t stride = (size_t)gridDim.x * kDdaThreads;
+        for (size_t v = w; v < nw; v += stride) out[v] = reduce_word<N, BF16>(b, chunk_off_bytes + v * 4);
+    } else {
+        if (w >= nw) return;
         out[w] = reduce_word<N, BF16>(b, chunk_off_bytes + w * 4);
+    }
+}
+
+template <int N, bool BF16>
+static hipError_t launch_tree_rs_n(const RankBufs& b, size_t off, size_t nw, uint32_t* out, hipStream_t stream) {
+    const size_t groups = (nw + kDdaThreads - 1) / kDdaThreads;
+    if (groups <= kMaxWordGroups)
+        return launch(dda_tree_rs_kernel<N, BF16, false>, dim3((unsigned)groups), dim3(kDdaThreads), 0, stream, b,
+                      off, nw, out);
+    return launch(dda_tree_rs_kernel<N, BF16, true>, dim3((unsigned)kMaxWordGroups), dim3(kDdaThreads), 0, stream, b,
+                  off, nw, out);
 }
 
 hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank, size_t n, void* out,
@@ -651,13 +677,11 @@ hipError_t launch_dda_tree_rs(const RankBufs& b, int bf16, int nranks, int rank,
     const size_t nw = chunk_bytes / 4;
     const size_t off = (size_t)rank * chunk_bytes;
     uint32_t* o = static_cast<uint32_t*>(out);
-    const size_t groups = (nw + kDdaThreads - 1) / kDdaThreads;
-    const dim3 grid((unsigned)(groups < kTreeMaxGroups ? groups : kTreeMaxGroups)), block(kDdaThreads);
     switch (nranks) {
-#define LPC_TREE_CASE(NR)                                                                            \
-    case NR:                                                                                         \
-        if (bf16) return launch(dda_tree_rs_kernel<NR, true>, grid, block, 0, stream, b, off, nw, o); \
-        return launch(dda_tree_rs_kernel<NR, false>, grid, block, 0, stream, b, off, nw, o);
+#define LPC_TREE_CASE(NR)                                                    \
+    case NR:                                                                 \
+        if (bf16) return launch_tree_rs_n<NR, true>(b, off, nw, o, stream); \
+        return launch_tree_rs_n<NR, false>(b, off, nw, o, stream);
         LPC_TREE_CASE(1) LPC_TREE_CASE(2) LPC_TREE_CASE(3) LPC_TREE_CASE(4)
         LPC_TREE_CASE(5) LPC_TREE_CASE(6) LPC_TREE_CASE(7) LPC_TREE_CASE(8)
 #undef LPC_TREE_CASE

@@ -90,9 +90,11 @@ typedef enum {
 } lpc_dtype;
 
 /* Largest element count accepted by any call: 2^32 elements (16 GiB of fp32).
- * The narrowest kernels give each lane 4 elements, and HIP takes at most
- * 2^31 - 1 lanes along a grid dimension, so every launch stays within that
- * limit; larger buffers go in several calls. */
+ * A launch takes at most 2^31 - 1 lanes along a grid dimension: the kernels
+ * give each lane 4 or more elements, except DDA flat and DDA tree's
+ * reduce-scatter (one 32-bit word a lane), which near this size cap their grid
+ * and let each lane take further words at the grid's stride.  Larger buffers
+ * go in several calls. */
 #define LPC_MAX_ELEMS ((size_t)1 << 32)
 
 /* ---------------------------------------------------------------------- */

@@ -39,8 +39,9 @@ def arr(*ptrs):
 def test_header_limits_match_binding():
     text = open(lpc.HEADER).read()
     assert re.search(r"#define LPC_MAX_ELEMS \(\(size_t\)1 << (\d+)\)", text).group(1) == "32"
-    # the narrowest kernels take 4 elements per lane; HIP accepts at most
-    # 2^31 - 1 lanes along one grid dimension
+    # the lane-vector kernels take 4 or more elements per lane; HIP accepts at
+    # most 2^31 - 1 lanes along one grid dimension (the word-wide DDA kernels
+    # cap their grid instead)
     assert MAX_ELEMS // 4 < 2 ** 31
 
 

@@ -701,22 +701,29 @@ def test_dda_tree_rs_guarded(dev, orc, bf16, N, n):
         assert bool((guard[C:] == -7.0).all()), "dda tree rs wrote past the chunk"
 
 
-def test_dda_tree_rs_at_the_largest_size(dev):
-    """One fp32 rank of n = LPC_MAX_ELEMS (16 GiB): a chunk of 2^32 words, more than one launch
-    has lanes for, so the grid's lanes take every grid-size-th word.  With one rank the reduce
-    is the identity; checked on words on both sides of every 1 GiB and 4,096 random ones."""
+@pytest.mark.parametrize("what", ["tree_rs_f32", "tree_rs_bf16", "flat_bf16"])
+def test_dda_word_kernels_at_the_largest_size(dev, what):
+    """One rank of n = LPC_MAX_ELEMS: 2^32 or 2^31 words, more than one launch has lanes for,
+    so the grid stops short and its lanes take every grid-size-th word.  With one rank the
+    reduce is the identity (bf16 -> fp32 -> bf16 is exact); checked on words on both sides of
+    every 1/16 of the buffer, the first and last ones and 4,096 random ones."""
     n = lpc.MAX_ELEMS
-    say("dda tree rs at n = %d, N = 1" % n)
+    dt = torch.float32 if what == "tree_rs_f32" else torch.bfloat16
+    say("%s at n = %d, N = 1" % (what, n))
     gen = torch.Generator(device=dev)
     gen.manual_seed(117)
-    x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32)
-    out = torch.zeros(n, dtype=torch.float32, device=dev)
-    lpc.dda_tree_reduce_scatter([x], 0, out)
+    x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32).to(dt)
+    out = torch.zeros(n, dtype=dt, device=dev)
+    if what == "flat_bf16":
+        lpc.dda_flat_reduce([x], out)
+    else:
+        lpc.dda_tree_reduce_scatter([x], 0, out)
     torch.cuda.synchronize()
     rng = np.random.Generator(np.random.PCG64(117))
     marks = [0, 1, n - 2, n - 1] + [k * (n // 16) + d for k in range(1, 16) for d in (-1, 0)]
     idx = torch.from_numpy(np.unique(np.concatenate([np.array(marks), rng.integers(0, n, 4096)]))).to(dev)
-    assert torch.equal(out[idx].view(torch.int32), x[idx].view(torch.int32)), "max-size tree reduce-scatter"
+    iv = torch.int32 if dt == torch.float32 else torch.int16
+    assert torch.equal(out[idx].view(iv), x[idx].view(iv)), "max-size %s" % what
     del x, out
     torch.cuda.empty_cache()
 
