@@ -51,8 +51,10 @@ the unfused reduce-scatter and all-gather, the one-quantization
 low-precision reduce-scatter, the DDA tree phases at 2 MiB bf16 per rank,
 the emulated 8-rank allreduce (low precision and DDA tree at 16 MiB, DDA
 flat at 64 KiB), the N=8 x 256 MiB bf16 fused launch and quantize, the fp32
-fused launch at 16, 32, 64 and 128 MiB per rank, and the all-to-all-v route,
-row quantize and dequantize at 16,384 x 7168 bf16.
+fused launch at 4, 8, 16, 32, 64 and 128 MiB per rank, and the all-to-all-v
+route, row quantize and dequantize at 16,384 x 7168 bf16.  Every
+bandwidth-sized line carries the plain streaming kernel at its bytes as its
+ceiling; DDA flat's lines also carry an empty launch of their grid.
 """
 from __future__ import annotations
 
